@@ -1,0 +1,172 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed-MoE FFN layer library (libmoe.so).
+ *
+ * The layer is the DeepSeek-V4-Flash-style routed mixture-of-experts FFN defined on the
+ * DeepSeek-V4.1-Flash native-tensor page ("Native 1017 DSpark draft on the NVLink pair"):
+ *   section 2 "Official semantics" - quantized linear, activation QDQ, Gate, Expert, MoE;
+ *   section 4 "Kernel contract"    - inputs, packed/expanded weight formats, per-(t, j) math, outputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer owned by the caller, unless stated otherwise
+ *   (the dims and weight-set structs themselves live in host memory). Tensors are dense, row-major,
+ *   16-byte aligned; the workspace is 256-byte aligned.
+ * - `stream` is a hipStream_t (NULL = the default stream). Work is only enqueued: no entry point
+ *   synchronizes, allocates device memory or copies device data to the host. Routing never leaves
+ *   the device.
+ * - Arguments are validated on the host before anything is launched; a failed check returns a
+ *   negative moe_status and enqueues nothing. There is no fallback path: an unsupported shape is
+ *   refused. A failing launch returns MOE_ERR_HIP; faults inside kernels surface at the caller's
+ *   next synchronization.
+ * - Launch geometry depends only on (dims, M), never on routed data.
+ * - A workspace must not be used by two calls in flight at the same time.
+ * - M = 0 is a valid empty call (returns MOE_OK, enqueues nothing).
+ *
+ * Supported domain: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of 128, 0 <= M <= 2^24,
+ * M * k <= 2^26, H * I <= 2^31. E8M0 scale bytes must be in 1..254 (255 is NaN; 0 is outside the
+ * supported range); E4M3 weight bytes must be finite (not 0x7F/0xFF).
+ *
+ * Data formats (section 2):
+ * - bf16: uint16 bit pattern. fp32: float.
+ * - MXFP4 matrix [rows, cols]: uint8 [rows, cols/2]; byte j of a row holds input 2j in the low nibble
+ *   and input 2j+1 in the high nibble; E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, bit 3 = sign;
+ *   one E8M0 scale byte per 32 inputs of a row, uint8 [rows, cols/32]; value = e2m1 * 2^(b-127).
+ * - FP8 matrix [rows, cols]: E4M3fn bytes uint8 [rows, cols]; one E8M0 byte per 32x32 block,
+ *   uint8 [rows/32, cols/32].
+ * - QDQ'd activations (x_q/x_s, h_q/h_s): E4M3 codes uint8 [rows, n] and E8M0 bytes [rows, n/32],
+ *   value = e4m3(code) * 2^(b-127); s = 2^ceil(log2(max(amax, 1e-4) / 448)) per 32 inputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null or misaligned pointer, negative size, bad dims       */
+#define MOE_ERR_UNSUPPORTED (-2) /* shape outside the supported domain                        */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace smaller than moe_workspace_bytes(dims, M)       */
+#define MOE_ERR_HIP (-4)         /* a kernel launch failed                                    */
+
+/* Layer dimensions (host struct). */
+typedef struct {
+  int32_t num_experts; /* E: routed experts                         */
+  int32_t hidden;      /* H: model width (x and output columns)     */
+  int32_t inter;       /* I: expert intermediate width              */
+  int32_t top_k;       /* k: experts per token                      */
+  float route_scale;   /* multiplies the normalised route weights   */
+} moe_dims;
+
+/* Routed experts in packed MXFP4 (section 1 table, section 2 formats). Host struct of device pointers. */
+typedef struct {
+  const uint8_t* w1; /* [E, I, H/2]  gate projection  */
+  const uint8_t* s1; /* [E, I, H/32]                  */
+  const uint8_t* w3; /* [E, I, H/2]  up projection    */
+  const uint8_t* s3; /* [E, I, H/32]                  */
+  const uint8_t* w2; /* [E, H, I/2]  down projection  */
+  const uint8_t* s2; /* [E, H, I/32]                  */
+} moe_mxfp4_experts;
+
+/* Routed experts expanded to bf16 (section 4 "expanded weights": exactly code * 2^(b-127)). */
+typedef struct {
+  const uint16_t* w1; /* [E, I, H] */
+  const uint16_t* w3; /* [E, I, H] */
+  const uint16_t* w2; /* [E, H, I] */
+} moe_bf16_experts;
+
+/* Shared expert in FP8 E4M3 with E8M0 32x32 block scales (section 1 table, section 2). */
+typedef struct {
+  const uint8_t* w1; /* [I, H]        */
+  const uint8_t* s1; /* [I/32, H/32]  */
+  const uint8_t* w3; /* [I, H]        */
+  const uint8_t* s3; /* [I/32, H/32]  */
+  const uint8_t* w2; /* [H, I]        */
+  const uint8_t* s2; /* [H/32, I/32]  */
+} moe_fp8_expert;
+
+/* Bytes of workspace the entry points need for up to max_tokens rows; 0 if dims are invalid.
+ * Holds the router logits, routing, QDQ'd x, permutation, QDQ'd h of every (token, slot), the
+ * per-slot bf16 expert outputs and the shared expert's intermediates. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status status);
+
+/* Router + activation QDQ (section 2 "Gate" and "Quantized linear").
+ * x bf16 [M, H] (raw, not QDQ'd), gate_w fp32 [E, H], gate_b fp32 [E] ->
+ * ids int32 [M, k]: the k largest sqrt(softplus(x W^T)) + bias, descending, ties to the lower id;
+ * rw fp32 [M, k]: route_scale * s[ids] / (sum_j s[ids_j] + 1e-20), the sum taken in slot order;
+ * x_q uint8 [M, H], x_s uint8 [M, H/32]: QDQ of x per 32 inputs (shared by all experts). */
+moe_status moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                     int32_t* ids, float* rw, uint8_t* x_q, uint8_t* x_s, void* ws, size_t ws_bytes, void* stream);
+
+/* Token-to-expert permutation: a stable counting sort of the M*k pairs p = t*k + j by ids[p].
+ * counts int32 [E]; offsets int32 [E+1] (exclusive prefix sum, offsets[E] = number of valid pairs);
+ * pairs int32 [M*k]: pair ids grouped by expert, ascending within an expert; inv int32 [M*k]
+ * (nullable): position of each pair in `pairs`; active int32 [E]: experts with counts > 0 in
+ * ascending order, then -1. Ids outside [0, E) are ignored. */
+moe_status moe_permute(const moe_dims* dims, int32_t M, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                       int32_t* pairs, int32_t* inv, int32_t* active, void* stream);
+
+/* Routed experts (section 4 math per (t, j)): for each pair p at sorted position q with expert e,
+ * g = bf16(x_hat w1[e]^T), u = bf16(x_hat w3[e]^T), h = rw[p] * silu(min(g, 10)) * clamp(u, -10, 10)
+ * in fp32, h16 = bf16(h), (h_q, h_s) = QDQ(h16), slot_out[p] = bf16(h_hat w2[e]^T).
+ * Exactly one of `packed` / `decoded` is non-NULL (the decoded-BF16 arm computes the same values
+ * from expanded weights). x_q/x_s from moe_route; rw [M*k]; offsets/pairs/active from moe_permute.
+ * slot_out bf16 [M*k, H] indexed by pair id. h_q uint8 [M*k, I] / h_s uint8 [M*k, I/32] indexed
+ * by sorted position: both NULL = kept in the workspace, or both given to receive them. */
+moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                          const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                          const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+                          uint16_t* slot_out, uint8_t* h_q, uint8_t* h_s, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* The two halves of moe_expert_ffn, for callers that time or schedule them separately.
+ * moe_expert_gemm1: h_q uint8 [M*k, I] and h_s uint8 [M*k, I/32] (rows = sorted positions) from
+ *   x_q/x_s: g, u, clamped SwiGLU times rw, bf16, QDQ per 32 (section 4 math up to hq).
+ * moe_expert_gemm2: slot_out bf16 [M*k, H] (rows = pair ids) = bf16(h_hat w2[e]^T).
+ * Same argument rules as moe_expert_ffn; no workspace. */
+moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                            const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                            const int32_t* offsets, const int32_t* pairs, const int32_t* active, uint8_t* h_q,
+                            uint8_t* h_s, void* stream);
+moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q, const uint8_t* h_s,
+                            const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
+                            const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+                            uint16_t* slot_out, void* stream);
+
+/* Shared expert (section 2 "Expert", FP8 weights, no route weight) on every row:
+ * shared_out bf16 [M, H] = bf16(QDQ(bf16(silu(min(g,10)) * clamp(u,-10,10))) w2^T). */
+moe_status moe_shared_expert(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                             const moe_fp8_expert* shared, uint16_t* shared_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Combine (section 2 "MoE"): out[t] = bf16(fp32 sum of slot_out[t*k + j] over the token's slots in
+ * ascending ids[t, j] order, then + shared_out[t] if shared_out is not NULL). out bf16 [M, H]. */
+moe_status moe_combine(const moe_dims* dims, int32_t M, const int32_t* ids, const uint16_t* slot_out,
+                       const uint16_t* shared_out, uint16_t* out, void* stream);
+
+/* The whole layer: moe_route -> moe_permute -> moe_expert_ffn -> (moe_shared_expert) -> moe_combine.
+ * Exactly one of packed / decoded is non-NULL; shared may be NULL. out bf16 [M, H].
+ * ids_out [M, k], rw_out [M, k] and shared_out [M, H] are optional (NULL = workspace only). */
+moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                       const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
+                       uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Expand one packed MXFP4 matrix (or a stack of them) to bf16: w uint8 [rows, cols/2], s uint8
+ * [rows, cols/32] -> out bf16 [rows, cols], exactly code * 2^(b-127) (section 4 "expanded weights").
+ * cols a multiple of 32, rows >= 0. */
+moe_status moe_expand_mxfp4(int64_t rows, int32_t cols, const uint8_t* w, const uint8_t* s, uint16_t* out,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

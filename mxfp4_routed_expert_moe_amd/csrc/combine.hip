@@ -1,0 +1,66 @@
+// Fixed-order combine of the routed experts (DeepSeek-V4.1-Flash native-tensor page, section 2
+// "MoE"): y = 0 in fp32; for the token's expert ids in ascending order, y += that expert's bf16
+// output (as fp32); then y += the shared expert's bf16 output; out = bf16(y). One token per block,
+// no atomics: the order of the adds is fixed by the ids, so the result is run-to-run identical.
+#include "kernels.h"
+#include "moe_device.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(int H, int k, const int32_t* __restrict__ ids,
+                                                      const uint16_t* __restrict__ slot_out,
+                                                      const uint16_t* __restrict__ shared_out,
+                                                      uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  // slots of this token sorted by ascending expert id (stable in slot order; k <= 8)
+  int order[8], key[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    order[j] = j;
+    key[j] = (j < k) ? ids[(size_t)t * k + j] : 0x7FFFFFFF;
+  }
+#pragma unroll
+  for (int a = 1; a < 8; ++a)
+#pragma unroll
+    for (int b = a; b > 0; --b)
+      if (key[b] < key[b - 1]) {
+        const int tk = key[b]; key[b] = key[b - 1]; key[b - 1] = tk;
+        const int to = order[b]; order[b] = order[b - 1]; order[b - 1] = to;
+      }
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r < k) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(slot_out + ((size_t)t * k + order[r]) * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = acc[2 * i] + bits_to_f32(v[i] << 16);
+          acc[2 * i + 1] = acc[2 * i + 1] + bits_to_f32(v[i] & 0xFFFF0000u);
+        }
+      }
+    }
+    if (shared_out) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(shared_out + (size_t)t * H + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = acc[2 * i] + bits_to_f32(v[i] << 16);
+        acc[2 * i + 1] = acc[2 * i + 1] + bits_to_f32(v[i] & 0xFFFF0000u);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = uint32_t(f32_to_bf16_rne(acc[2 * i])) | (uint32_t(f32_to_bf16_rne(acc[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
+  }
+}
+
+void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out, const uint16_t* shared_out,
+                    uint16_t* out, hipStream_t s) {
+  combine_kernel<<<dim3(M), dim3(256), 0, s>>>(H, k, ids, slot_out, shared_out, out);
+}
+
+}  // namespace moe

@@ -1,0 +1,64 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe; the public C ABI is include/moe.h).
+// Every launcher enqueues on the given stream, never synchronizes and never allocates; the caller
+// (moe_abi.cpp) has validated shapes, pointers and workspace sizes before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (route.hip) --------------------------------------------------------------------
+// fp32 logits [M, E] of the raw bf16 activations against the fp32 gate weight [E, H].
+void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
+                          hipStream_t s);
+// sqrt(softplus) scores, biased top-k, normalised route weights; plus the per-32 E4M3 QDQ of x.
+void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
+                              const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
+                              uint8_t* x_q, uint8_t* x_s, hipStream_t s);
+
+// ---- permutation (permute.hip) -------------------------------------------------------------
+// Stable counting sort of the M*k (token, slot) pairs by expert id.
+void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                    int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
+
+// ---- expert GEMMs (expert_gemm.hip) --------------------------------------------------------
+enum WeightFormat { W_MXFP4 = 0, W_FP8_BLOCK32 = 1, W_BF16 = 2 };
+
+struct GemmProblem {
+  // weights: GEMM1 uses wa = w1, wb = w3; GEMM2 uses wa = w2 (wb unused). Per-expert strides in
+  // elements of the storage type (bytes for MXFP4/FP8, bf16 elements for BF16).
+  const void* wa; const uint8_t* sa;
+  const void* wb; const uint8_t* sb;
+  long long w_expert_stride;   // storage elements per expert matrix
+  long long s_expert_stride;   // scale bytes per expert matrix
+  int N;                       // weight rows (output features)
+  int K;                       // inner dimension
+  // activations: E4M3 codes [rows, K] and E8M0 scales [rows, K/32]
+  const uint8_t* act_q; const uint8_t* act_s;
+  // routing: dense = one pseudo-expert over rows 0..M-1 in order (shared expert)
+  int dense; int M; int k;
+  const int32_t* offsets;      // [E + 1]
+  const int32_t* pairs;        // [M * k]: pair id t * k + j at each sorted position
+  const int32_t* active;       // [E]: active expert ids (ascending, -1 padded)
+  const float* rw;             // [M * k] route weight per pair (GEMM1, routed only)
+  int act_by_token;            // 1: activation row = token of the pair; 0: row = sorted position
+  // outputs
+  uint8_t* h_q; uint8_t* h_s;  // GEMM1: QDQ'd h codes [rows, N] and scales [rows, N/32]
+  uint16_t* out;               // GEMM2: bf16 [*, N]; row = pair id (routed) or token (dense)
+};
+// GEMM1: g = w1 x, u = w3 x -> bf16 -> SwiGLU (x rw) -> bf16 -> QDQ per 32 -> h_q, h_s
+void launch_gemm1_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
+// GEMM2: y = w2 h -> bf16 rows
+void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
+
+// ---- combine (combine.hip) -----------------------------------------------------------------
+void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,
+                    const uint16_t* shared_out, uint16_t* out, hipStream_t s);
+
+// ---- expansion of packed experts to bf16 (expand.hip) --------------------------------------
+void launch_expand_mxfp4(long long rows, int cols, const uint8_t* w, const uint8_t* sc, uint16_t* out,
+                         hipStream_t s);
+
+}  // namespace moe

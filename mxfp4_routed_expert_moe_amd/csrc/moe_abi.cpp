@@ -1,0 +1,355 @@
+// C ABI of libmoe (declared in include/moe.h): host-side validation, workspace layout and the
+// launch sequence of the routed-MoE layer. No entry point allocates, synchronizes or reads device
+// data; every check runs before the first launch and a refusal enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::GemmProblem;
+
+struct WsLayout {
+  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, h_q, h_s, slot, sh_q, sh_s, sh_out;
+  size_t total;
+};
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+WsLayout ws_layout(const moe_dims* d, int64_t M) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes, 256);
+    return o;
+  };
+  const size_t E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k, m = (size_t)M;
+  L.logits = take(m * E * 4);
+  L.ids = take(m * k * 4);
+  L.rw = take(m * k * 4);
+  L.x_q = take(m * H);
+  L.x_s = take(m * H / 32);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.pairs = take(m * k * 4);
+  L.inv = take(m * k * 4);
+  L.active = take(E * 4);
+  L.h_q = take(m * k * I);
+  L.h_s = take(m * k * I / 32);
+  L.slot = take(m * k * H * 2);
+  L.sh_q = take(m * I);
+  L.sh_s = take(m * I / 32);
+  L.sh_out = take(m * H * 2);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+inline bool al(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_dims(const moe_dims* d, int32_t M) {
+  if (d == nullptr || M < 0) return MOE_ERR_INVALID_ARG;
+  const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
+  if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || !std::isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
+  if (E > 256 || k > 8 || k > E) return MOE_ERR_UNSUPPORTED;
+  if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)H * I > (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (M > (1 << 24) || (int64_t)M * k > (int64_t(1) << 26)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_dims* d, int32_t M, const void* ws, size_t ws_bytes) {
+  if (!al(ws, 256)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ws_layout(d, M).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    const moe_status st_ = (expr);      \
+    if (st_ != MOE_OK) return st_;      \
+  } while (0)
+
+moe_status check_packed(const moe_mxfp4_experts* w) {
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !w->s1 || !w->s3 || !w->s2)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status check_decoded(const moe_bf16_experts* w) {
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status check_shared(const moe_fp8_expert* w) {
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !w->s1 || !w->s3 || !w->s2)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// ---- launch sequences (arguments already validated) ------------------------------------------
+void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, const float* gb, int32_t* ids,
+              float* rw, uint8_t* xq, uint8_t* xs, void* ws, hipStream_t s) {
+  const WsLayout L = ws_layout(d, M);
+  float* logits = at<float>(ws, L.logits);
+  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, s);
+  moe::launch_router_select_qdq(M, d->hidden, d->num_experts, d->top_k, d->route_scale, logits, gb, x, ids, rw, xq,
+                                xs, s);
+}
+
+// GEMM1: I rows of w1 and w3 over H inputs; activation row = token of the pair; output h rows at
+// sorted positions.
+void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
+              const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
+              const int32_t* active, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+  const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
+  const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
+  GemmProblem p{};
+  p.dense = 0; p.M = M; p.k = k;
+  p.offsets = offsets; p.pairs = pairs; p.active = active; p.rw = rw;
+  moe::WeightFormat f;
+  if (packed) {
+    f = moe::W_MXFP4;
+    p.wa = packed->w1; p.sa = packed->s1; p.wb = packed->w3; p.sb = packed->s3;
+    p.w_expert_stride = (long long)I * H / 2; p.s_expert_stride = (long long)I * H / 32;
+  } else {
+    f = moe::W_BF16;
+    p.wa = decoded->w1; p.sa = nullptr; p.wb = decoded->w3; p.sb = nullptr;
+    p.w_expert_stride = (long long)I * H; p.s_expert_stride = 0;
+  }
+  p.N = I; p.K = H;
+  p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
+  p.h_q = hq; p.h_s = hs;
+  moe::launch_gemm1_small(f, p, max_active, s);
+}
+
+// GEMM2: H rows of w2 over I inputs; activation row = sorted position; output row = pair id.
+void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, const moe_mxfp4_experts* packed,
+              const moe_bf16_experts* decoded, const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+              uint16_t* slot, hipStream_t s) {
+  const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
+  const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
+  GemmProblem q{};
+  q.dense = 0; q.M = M; q.k = k;
+  q.offsets = offsets; q.pairs = pairs; q.active = active; q.rw = nullptr;
+  moe::WeightFormat f;
+  if (packed) {
+    f = moe::W_MXFP4;
+    q.wa = packed->w2; q.sa = packed->s2;
+    q.w_expert_stride = (long long)H * I / 2; q.s_expert_stride = (long long)H * I / 32;
+  } else {
+    f = moe::W_BF16;
+    q.wa = decoded->w2; q.sa = nullptr;
+    q.w_expert_stride = (long long)H * I; q.s_expert_stride = 0;
+  }
+  q.N = H; q.K = I;
+  q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
+  q.out = slot;
+  moe::launch_gemm2_small(f, q, max_active, s);
+}
+
+void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
+                   const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
+                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+  do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, s);
+  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, s);
+}
+
+void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_fp8_expert* sh,
+               uint8_t* shq, uint8_t* shs, uint16_t* out, hipStream_t s) {
+  const int H = d->hidden, I = d->inter;
+  GemmProblem p{};
+  p.dense = 1; p.M = M; p.k = 1;
+  p.wa = sh->w1; p.sa = sh->s1; p.wb = sh->w3; p.sb = sh->s3;
+  p.w_expert_stride = 0; p.s_expert_stride = 0;
+  p.N = I; p.K = H;
+  p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
+  p.h_q = shq; p.h_s = shs;
+  moe::launch_gemm1_small(moe::W_FP8_BLOCK32, p, 1, s);
+  GemmProblem q = p;
+  q.wa = sh->w2; q.sa = sh->s2; q.wb = nullptr; q.sb = nullptr;
+  q.N = H; q.K = I;
+  q.act_q = shq; q.act_s = shs; q.act_by_token = 0;
+  q.out = out;
+  moe::launch_gemm2_small(moe::W_FP8_BLOCK32, q, 1, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims, max_tokens) != MOE_OK) return 0;
+  return ws_layout(dims, max_tokens).total;
+}
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+moe_status moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                     int32_t* ids, float* rw, uint8_t* x_q, uint8_t* x_s, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(ids, 4) || !al(rw, 4) || !al(x_q, 16) || !x_s)
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  do_route(dims, M, x, gate_w, gate_b, ids, rw, x_q, x_s, ws, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_permute(const moe_dims* dims, int32_t M, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                       int32_t* pairs, int32_t* inv, int32_t* active, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  if (!al(ids, 4) || !al(counts, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4)) return MOE_ERR_INVALID_ARG;
+  if (inv != nullptr && !al(inv, 4)) return MOE_ERR_INVALID_ARG;
+  moe::launch_permute(M * dims->top_k, dims->num_experts, ids, counts, offsets, pairs, inv, active,
+                      static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                          const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                          const int32_t* offsets, const int32_t* pairs, const int32_t* active, uint16_t* slot_out,
+                          uint8_t* h_q, uint8_t* h_s, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (!al(x_q, 16) || !x_s || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
+    return MOE_ERR_INVALID_ARG;
+  if ((h_q == nullptr) != (h_s == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (h_q != nullptr && !al(h_q, 16)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  const WsLayout L = ws_layout(dims, M);
+  if (h_q == nullptr) {
+    h_q = at<uint8_t>(ws, L.h_q);
+    h_s = at<uint8_t>(ws, L.h_s);
+  }
+  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s,
+                static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                            const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                            const int32_t* offsets, const int32_t* pairs, const int32_t* active, uint8_t* h_q,
+                            uint8_t* h_s, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (!al(x_q, 16) || !x_s || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(h_q, 16) ||
+      !h_s)
+    return MOE_ERR_INVALID_ARG;
+  do_gemm1(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, h_q, h_s, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q, const uint8_t* h_s,
+                            const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
+                            const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+                            uint16_t* slot_out, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (!al(h_q, 16) || !h_s || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
+    return MOE_ERR_INVALID_ARG;
+  do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_shared_expert(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                             const moe_fp8_expert* shared, uint16_t* shared_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  MOE_TRY(check_shared(shared));
+  if (!al(x_q, 16) || !x_s || !al(shared_out, 16)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  const WsLayout L = ws_layout(dims, M);
+  do_shared(dims, M, x_q, x_s, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), shared_out,
+            static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_combine(const moe_dims* dims, int32_t M, const int32_t* ids, const uint16_t* slot_out,
+                       const uint16_t* shared_out, uint16_t* out, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  if (!al(ids, 4) || !al(slot_out, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (shared_out != nullptr && !al(shared_out, 16)) return MOE_ERR_INVALID_ARG;
+  moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot_out, shared_out, out, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                       const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
+                       uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (shared != nullptr) MOE_TRY(check_shared(shared));
+  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  if ((ids_out && !al(ids_out, 4)) || (rw_out && !al(rw_out, 4)) || (shared_out && !al(shared_out, 16)))
+    return MOE_ERR_INVALID_ARG;
+  if (shared_out != nullptr && shared == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const WsLayout L = ws_layout(dims, M);
+  int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
+  float* rw = rw_out ? rw_out : at<float>(ws, L.rw);
+  uint8_t* xq = at<uint8_t>(ws, L.x_q);
+  uint8_t* xs = at<uint8_t>(ws, L.x_s);
+  do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pairs = at<int32_t>(ws, L.pairs);
+  int32_t* active = at<int32_t>(ws, L.active);
+  moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
+                      at<int32_t>(ws, L.inv), active, s);
+  uint16_t* slot = at<uint16_t>(ws, L.slot);
+  do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, at<uint8_t>(ws, L.h_q),
+                at<uint8_t>(ws, L.h_s), s);
+  uint16_t* sh_out = nullptr;
+  if (shared != nullptr) {
+    sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
+    do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, s);
+  }
+  moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+  return launched();
+}
+
+moe_status moe_expand_mxfp4(int64_t rows, int32_t cols, const uint8_t* w, const uint8_t* s, uint16_t* out,
+                            void* stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!al(w, 16) || !s || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  moe::launch_expand_mxfp4(rows, cols, w, s, out, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+}  // extern "C"

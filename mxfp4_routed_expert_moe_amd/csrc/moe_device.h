@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels of the routed-MoE layer.
+//
+// Number formats follow the DeepSeek-V4.1-Flash native-tensor page, section 2 "Official semantics":
+// E2M1 nibbles (low nibble = even input), E8M0 scales 2^(b-127), FP8 E4M3 (OCP "e4m3fn"), bf16 with
+// round-to-nearest-even at every rounding point.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bits_to_f32(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = f32_to_bits(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// fp32 -> the bf16 value it rounds to, as an fp32
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16_rne(f)); }
+
+// E8M0 byte -> fp32 scale 2^(b-127); bytes 1..254 are exact normal fp32 values
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return bits_to_f32((b & 0xFFu) << 23); }
+
+// Activation QDQ scale (section 2, act_quant with a ue8m0 scale): E = ceil(log2(fp32(max(amax, 1e-4)
+// * fp32(1/448)))) read from the fp32 bits. Returns E; the stored E8M0 byte is E + 127.
+__device__ __forceinline__ int qdq_exponent(float amax) {
+  float a = fmaxf(amax, 1e-4f);
+  float v = a * (1.0f / 448.0f);
+  uint32_t u = f32_to_bits(v);
+  int e = int((u >> 23) & 0xFFu) - 127;
+  return e + ((u & 0x7FFFFFu) != 0u);
+}
+
+// 2^-E as an exact fp32 (E in [-126, 126])
+__device__ __forceinline__ float exp2_neg(int E) { return bits_to_f32(uint32_t(127 - E) << 23); }
+
+// fp32 value v with |v| <= 448 -> E4M3fn code, round to nearest even, subnormals kept, sign of zero kept.
+__device__ __forceinline__ uint32_t e4m3_encode_rne(float v) {
+  uint32_t u = f32_to_bits(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {                       // |v| < 2^-6: subnormal, quantum 2^-9
+    float m = __builtin_rintf(bits_to_f32(a) * 512.0f);
+    code = uint32_t(m);                          // 0..8 (8 is the smallest normal, code 0x08)
+  } else {                                       // round the fp32 mantissa to 3 bits
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);              // rebias exponent 127 -> 7
+  }
+  return code | sign;
+}
+
+// QDQ of one value given the block exponent E: clamp(x / 2^E, +-448) -> E4M3 code
+__device__ __forceinline__ uint32_t qdq_code(float x, float inv_scale) {
+  float q = x * inv_scale;                       // exact: power-of-two scaling
+  q = fminf(fmaxf(q, -448.0f), 448.0f);
+  return e4m3_encode_rne(q);
+}
+
+// Packed FP4 byte -> two bf16 (low nibble first) times the E8M0 scale, via the gfx950 converter
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t packed4, float scale) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed4, scale, BYTE);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two E4M3 codes (word WORD of a dword) -> two bf16 times the scale
+template <bool WORD>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed8, float scale) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed8, scale, WORD);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// SwiGLU of the routed/shared expert (section 2 "Expert", section 4 math): g and u are the
+// bf16-rounded linear outputs; u is clamped to [-10, 10] and g to at most 10; then
+// h = (g / (1 + exp(-g))) * u in fp32, times the route weight rw (1 for the shared expert).
+__device__ __forceinline__ float swiglu(float g, float u, float rw, bool weighted) {
+  g = fminf(g, 10.0f);
+  u = fminf(fmaxf(u, -10.0f), 10.0f);
+  float e = expf(-g);                            // full-precision exp (ROCm device library)
+  float d = 1.0f + e;
+  float h = (g / d) * u;
+  if (weighted) h = rw * h;
+  return h;
+}
+
+}  // namespace moe

@@ -1,0 +1,78 @@
+// Token-to-expert permutation: a stable counting sort of the M*k (token, slot) pairs by expert id.
+//
+// The expert GEMMs process the rows of one expert together (the grouped layout of the gfx90a paper,
+// section 7.1, and the route-direct chain of the Arc B70 page); the order inside an expert is
+// ascending pair id t*k + j, so results never depend on scheduling. No global atomics and no
+// in-kernel counter resets: block e counts with LDS atomics (integer, order-free) and compacts the
+// pairs of expert e with wave ballots.
+#include "kernels.h"
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kPermWaves = 16;
+
+__global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32_t* __restrict__ ids,
+                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
+                                                       int32_t* __restrict__ active) {
+  __shared__ int hist[256];
+  __shared__ int wave_cnt[kPermWaves];
+  __shared__ int base_off;
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  // each wave owns a contiguous segment of the pair list (a multiple of 64 long)
+  const int seg = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;
+  const int beg = wave * seg, end = min(P, beg + seg);
+  int mine = 0;
+  for (int i = beg + lane; i < beg + seg; i += 64) {
+    int v = -1;
+    if (i < end) v = ids[i];
+    const bool ok = v >= 0 && v < E;
+    if (ok) atomicAdd(&hist[v], 1);
+    mine += __popcll(__ballot(ok && v == e));
+  }
+  if (lane == 0) wave_cnt[wave] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    int off = 0;
+    for (int j = 0; j < e; ++j) off += hist[j];
+    base_off = off;
+    counts[e] = hist[e];
+    offsets[e] = off;
+    if (e == 0) {
+      int tot = 0, na = 0;
+      for (int j = 0; j < E; ++j) {
+        tot += hist[j];
+        if (hist[j] > 0) active[na++] = j;
+      }
+      for (int j = na; j < E; ++j) active[j] = -1;
+      offsets[E] = tot;
+    }
+  }
+  __syncthreads();
+  int base = base_off;
+  for (int w = 0; w < wave; ++w) base += wave_cnt[w];
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i = beg + lane; i < beg + seg; i += 64) {
+    int v = -1;
+    if (i < end) v = ids[i];
+    const bool hit = (v == e);
+    const unsigned long long m = __ballot(hit);
+    if (hit) {
+      const int pos = base + __popcll(m & below);
+      pairs[pos] = i;
+      if (inv) inv[i] = pos;
+    }
+    base += __popcll(m);
+  }
+}
+
+void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs,
+                    int32_t* inv, int32_t* active, hipStream_t s) {
+  permute_kernel<<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+}
+
+}  // namespace moe
