@@ -1,0 +1,267 @@
+"""Throughput of the routed-MoE FFN layer (MXFP4 experts) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_m8] [--replicas R]
+                    [--no-prefill] [--no-cpu-baseline]
+
+A step is one call of ``moe_forward`` (router + activation QDQ, permutation, grouped w1/w3 GEMM with
+SwiGLU and QDQ of h, grouped w2 GEMM, fixed-order combine) over one batch of seeded synthetic tokens.
+Inputs are resident in HBM before the timed region starts. The expert weights exist in R replicas and
+step i uses replica i mod R, so the 256 MB last-level cache cannot serve them from a previous step.
+
+Printed: one JSON line. ``value`` is tokens/s of the M=8 decode-width layer (hidden 5120, 128 MXFP4
+experts, intermediate 2304, top-6). ``roofline`` describes the dominant kernel, the grouped w1/w3 GEMM.
+``prefill`` holds the same figures for the M=8192 prefill layer. ``cpu_baseline`` is the CPU oracle timed
+on a bounded sample of the decode workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (E4M3 x E2M1 issues at the FP8 rate)
+
+WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m8192": 3,
+             "prefill_shared_skew_m2048": 4}
+
+
+def _bytes_per_expert(cfg):
+    """Packed MXFP4 bytes (codes + E8M0 scales) of one expert: (w1 + w3, w2)."""
+    H, I = cfg.H, cfg.I
+    w13 = 2 * (I * H // 2 + I * H // 32)
+    w2 = H * I // 2 + H * I // 32
+    return w13, w2
+
+
+def _flops_per_pair(cfg):
+    """Multiply-add flops of one (token, expert) assignment: (w1 + w3, w2)."""
+    return 2 * 2 * cfg.I * cfg.H, 2 * cfg.H * cfg.I
+
+
+class Layer:
+    """Device-resident inputs of one workload with R weight replicas, plus output buffers."""
+
+    def __init__(self, cid: int, replicas: int):
+        import numpy as np
+        import torch
+
+        import mxfp4_routed_expert_moe_amd as moe
+        import synth
+
+        self.moe, self.torch, self.np = moe, torch, np
+        self.cfg = cfg = synth.get_config(cid)
+        inp = synth.make_inputs(cfg)
+        self.digest = synth.digest({k: v for k, v in inp.items() if k in ("x", "gate_w", "gate_b", "w1", "w2")})
+
+        def up(a):
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+        self.x, self.gate_w, self.gate_b = up(inp["x"]), up(inp["gate_w"]), up(inp["gate_b"])
+        first = {n: up(inp[n]) for n in ("w1", "s1", "w3", "s3", "w2", "s2")}
+        self.experts = [moe.MXFP4Experts(**first)]
+        for _ in range(1, replicas):
+            self.experts.append(moe.MXFP4Experts(**{n: t.clone() for n, t in first.items()}))
+        self.shared = None
+        if cfg.shared:
+            self.shared = moe.FP8Expert(*(up(inp[n]) for n in ("sw1", "ss1", "sw3", "ss3", "sw2", "ss2")))
+        del inp
+        M, k, H, I, E = cfg.M, cfg.k, cfg.H, cfg.I, cfg.E
+        self.dims = moe.Dims(E, H, I, k, cfg.route_scale)
+        self.ws = moe.workspace(self.dims, M)
+        dev = dict(device="cuda")
+        self.out = torch.empty((M, H), dtype=torch.int16, **dev)
+        self.ids = torch.empty((M, k), dtype=torch.int32, **dev)
+        self.rw = torch.empty((M, k), dtype=torch.float32, **dev)
+        # buffers of the split entry points (kernel-level timing)
+        self.xq = torch.empty((M, H), dtype=torch.uint8, **dev)
+        self.xs = torch.empty((M, H // 32), dtype=torch.uint8, **dev)
+        self.counts = torch.empty(E, dtype=torch.int32, **dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, **dev)
+        self.pairs = torch.empty(M * k, dtype=torch.int32, **dev)
+        self.active = torch.empty(E, dtype=torch.int32, **dev)
+        self.hq = torch.empty((M * k, I), dtype=torch.uint8, **dev)
+        self.hs = torch.empty((M * k, I // 32), dtype=torch.uint8, **dev)
+        self.slot = torch.empty((M * k, H), dtype=torch.int16, **dev)
+        self.shared_out = torch.empty((M, H), dtype=torch.int16, **dev) if self.shared is not None else None
+
+    def step(self, i: int):
+        self.moe.moe_forward(self.dims, self.x, self.gate_w, self.gate_b, self.experts[i % len(self.experts)], None,
+                             self.shared, self.out, self.ids, self.rw, None, self.ws)
+
+    def split_step(self, i: int, ev):
+        """The same layer through the split entry points, with events between the kernels."""
+        m, w = self.moe, self.experts[i % len(self.experts)]
+        ev[0].record()
+        m.moe_route(self.dims, self.x, self.gate_w, self.gate_b, self.ids, self.rw, self.xq, self.xs, self.ws)
+        ev[1].record()
+        m.moe_permute(self.dims, self.ids, self.counts, self.offsets, self.pairs, None, self.active)
+        ev[2].record()
+        m.moe_expert_gemm1(self.dims, self.xq, self.xs, w, None, self.rw, self.offsets, self.pairs, self.active,
+                           self.hq, self.hs)
+        ev[3].record()
+        m.moe_expert_gemm2(self.dims, self.cfg.M, self.hq, self.hs, w, None, self.offsets, self.pairs, self.active,
+                           self.slot)
+        ev[4].record()
+        if self.shared is not None:
+            m.moe_shared_expert(self.dims, self.xq, self.xs, self.shared, self.shared_out, self.ws)
+        ev[5].record()
+        m.moe_combine(self.dims, self.ids, self.slot, self.shared_out, self.out)
+        ev[6].record()
+
+    def distinct_experts(self) -> int:
+        return int(self.torch.unique(self.ids).numel())
+
+
+def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
+    import torch
+
+    L = Layer(cid, replicas)
+    cfg = L.cfg
+    for i in range(warmup):
+        L.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L.step(warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    D = L.distinct_experts()
+
+    # kernel-level times: events between the split entry points, on the stream they launch on
+    names = ["route", "permute", "gemm1", "gemm2", "shared", "combine"]
+    tot = [0.0] * len(names)
+    n_k = max(steps, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_k)]
+    for i in range(warmup):
+        L.split_step(i, evs[0])
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        L.split_step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    for ev in evs:
+        for j in range(len(names)):
+            tot[j] += ev[j].elapsed_time(ev[j + 1])
+    kern_us = {n: 1e3 * t / n_k for n, t in zip(names, tot)}
+    if L.shared is None:
+        kern_us.pop("shared")
+
+    w13_b, w2_b = _bytes_per_expert(cfg)
+    f13, f2 = _flops_per_pair(cfg)
+    P = cfg.M * cfg.k
+    gemm1_bytes = D * w13_b + cfg.M * (cfg.H + cfg.H // 32) + P * (cfg.I + cfg.I // 32)
+    gemm1_flops = P * f13
+    layer_bytes = D * (w13_b + w2_b) + cfg.E * cfg.H * 4
+    res = dict(workload=cfg.name, M=cfg.M, ms_per_step=ms, tokens_per_s=cfg.M / (ms * 1e-3), distinct_experts=D,
+               kernel_us=kern_us, layer_weight_bytes=layer_bytes,
+               layer_hbm_frac=(layer_bytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9),
+               layer_tflops=(P * (f13 + f2)) / (ms * 1e-3) / 1e12, replicas=replicas, inputs_sha256=L.digest)
+    g1 = kern_us["gemm1"] * 1e-6
+    if cfg.M <= 64:
+        ach = gemm1_bytes / g1 / 1e9
+        res["roofline"] = dict(kernel="expert_gemm1 (w1/w3 + SwiGLU + QDQ)", bound="hbm", achieved=round(ach, 1),
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                               algorithmic_bytes=gemm1_bytes, avg_us=round(kern_us["gemm1"], 2))
+    else:
+        ach = gemm1_flops / g1 / 1e12
+        res["roofline"] = dict(kernel="expert_gemm1 (w1/w3 + SwiGLU + QDQ)", bound="mfma", achieved=round(ach, 1),
+                               peak=MFMA_FP8_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
+                               traffic=None, algorithmic_flops=gemm1_flops, avg_us=round(kern_us["gemm1"], 2))
+    del L
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_tokens: int = 1) -> dict:
+    """The CPU oracle, as it stands, on the first token(s) of the decode workload."""
+    import synth
+    from oracle import moe as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: the BLAS pool size is unknown, report the host count
+        cores = os.cpu_count() or 1
+    cfg = synth.get_config(1)
+    inp = synth.make_inputs(cfg)
+    toks = list(range(budget_tokens))
+    t0 = time.perf_counter()
+    O.moe_forward(inp, cfg, tokens=toks)
+    dt = time.perf_counter() - t0
+    return dict(value=round(len(toks) / dt, 5), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{len(toks)} token(s) of decode_m8 (router, QDQ, its {cfg.k} experts decoded from MXFP4, "
+                       f"fp64 dot products, combine); {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_m8", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the layer is measured on a single MI355X (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_routed_expert_moe_amd  # noqa: F401  (fails loudly if libmoe.so is missing)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas)
+    print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step, kernels {main_res['kernel_us']}",
+          file=sys.stderr, flush=True)
+    prefill = None
+    if not args.no_prefill and args.workload != "prefill_m8192":
+        p = measure(3, max(3, args.steps // 10), max(1, args.warmup // 5), 2)
+        print(f"# {p['workload']}: {p['ms_per_step']:.3f} ms/step, kernels {p['kernel_us']}", file=sys.stderr,
+              flush=True)
+        prefill = dict(workload=p["workload"], value=round(p["tokens_per_s"], 1), unit="tokens/s",
+                       ms_per_step=round(p["ms_per_step"], 4), kernel_us={k: round(v, 1) for k, v in
+                                                                          p["kernel_us"].items()},
+                       layer_tflops=round(p["layer_tflops"], 1), roofline=p["roofline"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+    r = main_res
+    line = {
+        "metric": "MoE-layer tokens/s at M=8 and M=8192; % of HBM BW / MXFP4 MFMA roofline",
+        "value": round(r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 x mxfp4 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded)",
+        "config": {"workload": r["workload"], "M": r["M"], "hidden": 5120, "experts": 128, "inter": 2304,
+                   "top_k": 6, "distinct_experts": r["distinct_experts"], "weight_replicas": r["replicas"],
+                   "parallelism": "none (1 GPU)"},
+        "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()},
+        "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
+        "roofline": r["roofline"],
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
