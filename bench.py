@@ -106,10 +106,10 @@ class Layer:
         m.moe_permute(self.dims, self.ids, self.counts, self.offsets, self.pairs, None, self.active)
         ev[2].record()
         m.moe_expert_gemm1(self.dims, self.xq, self.xs, w, None, self.rw, self.offsets, self.pairs, self.active,
-                           self.hq, self.hs)
+                           self.hq, self.hs, self.ws)
         ev[3].record()
         m.moe_expert_gemm2(self.dims, self.cfg.M, self.hq, self.hs, w, None, self.offsets, self.pairs, self.active,
-                           self.slot)
+                           self.slot, self.ws)
         ev[4].record()
         if self.shared is not None:
             m.moe_shared_expert(self.dims, self.xq, self.xs, self.shared, self.shared_out, self.ws)

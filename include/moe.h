@@ -130,15 +130,16 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
  * moe_expert_gemm1: h_q uint8 [M*k, I] and h_s uint8 [M*k, I/32] (rows = sorted positions) from
  *   x_q/x_s: g, u, clamped SwiGLU times rw, bf16, QDQ per 32 (section 4 math up to hq).
  * moe_expert_gemm2: slot_out bf16 [M*k, H] (rows = pair ids) = bf16(h_hat w2[e]^T).
- * Same argument rules as moe_expert_ffn; no workspace. */
+ * Same argument rules as moe_expert_ffn. The workspace (moe_workspace_bytes(dims, M)) holds the
+ * row-tile list the prefill-width kernels build from `offsets`; each call builds its own. */
 moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
                             const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
                             const int32_t* offsets, const int32_t* pairs, const int32_t* active, uint8_t* h_q,
-                            uint8_t* h_s, void* stream);
+                            uint8_t* h_s, void* ws, size_t ws_bytes, void* stream);
 moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q, const uint8_t* h_s,
                             const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
                             const int32_t* offsets, const int32_t* pairs, const int32_t* active,
-                            uint16_t* slot_out, void* stream);
+                            uint16_t* slot_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Shared expert (section 2 "Expert", FP8 weights, no route weight) on every row:
  * shared_out bf16 [M, H] = bf16(QDQ(bf16(silu(min(g,10)) * clamp(u,-10,10))) w2^T). */

@@ -68,10 +68,10 @@ lib.moe_expert_ffn.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINT
                                _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_expert_ffn.restype = _I32
 lib.moe_expert_gemm1.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
-                                 _P, _P, _P, _P, _P, _P, _P]
+                                 _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_expert_gemm1.restype = _I32
 lib.moe_expert_gemm2.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
-                                 _P, _P, _P, _P, _P]
+                                 _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_expert_gemm2.restype = _I32
 lib.moe_shared_expert.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_FP8), _P, _P, _SZ, _P]
 lib.moe_shared_expert.restype = _I32
@@ -215,24 +215,24 @@ def moe_expert_ffn(dims: Dims, x_q, x_s, packed: MXFP4Experts | None, decoded: B
 
 
 def moe_expert_gemm1(dims: Dims, x_q, x_s, packed: MXFP4Experts | None, decoded: BF16Experts | None, rw, offsets,
-                     pairs, active, h_q, h_s, stream=None):
+                     pairs, active, h_q, h_s, ws, stream=None):
     M = x_q.shape[0]
     pk = ctypes.byref(packed.c()) if packed is not None else None
     dc = ctypes.byref(decoded.c()) if decoded is not None else None
     st = lib.moe_expert_gemm1(ctypes.byref(dims.c()), M, _ptr(x_q, torch.uint8), _ptr(x_s, torch.uint8), pk, dc,
                               _ptr(rw, torch.float32), _ptr(offsets, torch.int32), _ptr(pairs, torch.int32),
                               _ptr(active, torch.int32), _ptr(h_q, torch.uint8), _ptr(h_s, torch.uint8),
-                              _stream(stream))
+                              _ptr(ws, torch.uint8), ws.numel(), _stream(stream))
     _check(st, "moe_expert_gemm1")
 
 
 def moe_expert_gemm2(dims: Dims, M: int, h_q, h_s, packed: MXFP4Experts | None, decoded: BF16Experts | None, offsets,
-                     pairs, active, slot_out, stream=None):
+                     pairs, active, slot_out, ws, stream=None):
     pk = ctypes.byref(packed.c()) if packed is not None else None
     dc = ctypes.byref(decoded.c()) if decoded is not None else None
     st = lib.moe_expert_gemm2(ctypes.byref(dims.c()), M, _ptr(h_q, torch.uint8), _ptr(h_s, torch.uint8), pk, dc,
                               _ptr(offsets, torch.int32), _ptr(pairs, torch.int32), _ptr(active, torch.int32),
-                              _ptr(slot_out, _BF), _stream(stream))
+                              _ptr(slot_out, _BF), _ptr(ws, torch.uint8), ws.numel(), _stream(stream))
     _check(st, "moe_expert_gemm2")
 
 

@@ -10,7 +10,9 @@
 namespace moe {
 
 // ---- router (route.hip) --------------------------------------------------------------------
-// fp32 logits [M, E] of the raw bf16 activations against the fp32 gate weight [E, H].
+// fp32 logits of the raw bf16 activations against the fp32 gate weight [E, H], as
+// router_logit_parts(M, H) partial planes [parts, M, E] (summed in order by the select kernel).
+int router_logit_parts(int M, int H);
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
                           hipStream_t s);
 // sqrt(softplus) scores, biased top-k, normalised route weights; plus the per-32 E4M3 QDQ of x.
@@ -52,6 +54,18 @@ struct GemmProblem {
 void launch_gemm1_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
 // GEMM2: y = w2 h -> bf16 rows
 void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
+
+// ---- expert GEMMs on the block-scaled matrix cores (expert_mfma.hip) ---------------------------
+// Upper bound of the row-tile list for P (token, slot) pairs over E experts.
+int mfma_max_tiles(int P, int E);
+// Row-tile list from the expert offsets: tile_e [max_tiles] (-1 past the end), tile_r0 [max_tiles].
+void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0,
+                     hipStream_t s);
+// Same problems as the *_small launchers (MXFP4 or FP8 weights only); routed problems take the tile list.
+void launch_gemm1_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
+                       const int32_t* tile_r0, hipStream_t s);
+void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
+                       const int32_t* tile_r0, hipStream_t s);
 
 // ---- combine (combine.hip) -----------------------------------------------------------------
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,

@@ -15,7 +15,8 @@ namespace {
 using moe::GemmProblem;
 
 struct WsLayout {
-  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, h_q, h_s, slot, sh_q, sh_s, sh_out;
+  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, h_q, h_s, slot, sh_q, sh_s,
+      sh_out;
   size_t total;
 };
 
@@ -30,7 +31,10 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
     return o;
   };
   const size_t E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k, m = (size_t)M;
-  L.logits = take(m * E * 4);
+  // router logits: partial planes at small M; sized so the total never shrinks as M grows (a
+  // workspace sized for max_tokens serves every M <= max_tokens)
+  const size_t small_rows = std::min<size_t>(m, 64) * (size_t)moe::router_logit_parts(1, (int)H);
+  L.logits = take(std::max(m, small_rows) * E * 4);
   L.ids = take(m * k * 4);
   L.rw = take(m * k * 4);
   L.x_q = take(m * H);
@@ -40,6 +44,8 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.pairs = take(m * k * 4);
   L.inv = take(m * k * 4);
   L.active = take(E * 4);
+  L.tile_e = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
+  L.tile_r0 = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
   L.h_q = take(m * k * I);
   L.h_s = take(m * k * I / 32);
   L.slot = take(m * k * H * 2);
@@ -100,6 +106,31 @@ moe_status check_shared(const moe_fp8_expert* w) {
 }
 
 // ---- launch sequences (arguments already validated) ------------------------------------------
+// Kernel variant: a pure function of (dims, M). The block-scaled MFMA grouped GEMM once the experts
+// hold 32 rows on average (prefill); the weight-streaming kernel at decode width and for the
+// decoded-BF16 arm.
+inline bool routed_mfma(const moe_dims* d, int M, const moe_mxfp4_experts* packed) {
+  return packed != nullptr && (int64_t)M * d->top_k >= 32 * (int64_t)d->num_experts;
+}
+inline bool shared_mfma(int M) { return M > 64; }
+
+struct TileMap {
+  int max_tiles = 0;
+  const int32_t* tile_e = nullptr;
+  const int32_t* tile_r0 = nullptr;
+};
+
+TileMap make_tile_map(const moe_dims* d, int M, const int32_t* offsets, void* ws, hipStream_t s) {
+  const WsLayout L = ws_layout(d, M);
+  TileMap t;
+  t.max_tiles = moe::mfma_max_tiles(M * d->top_k, d->num_experts);
+  int32_t* te = at<int32_t>(ws, L.tile_e);
+  int32_t* tr = at<int32_t>(ws, L.tile_r0);
+  moe::launch_tile_map(d->num_experts, t.max_tiles, offsets, te, tr, s);
+  t.tile_e = te;
+  t.tile_r0 = tr;
+  return t;
+}
 void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, const float* gb, int32_t* ids,
               float* rw, uint8_t* xq, uint8_t* xs, void* ws, hipStream_t s) {
   const WsLayout L = ws_layout(d, M);
@@ -113,7 +144,7 @@ void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, cons
 // sorted positions.
 void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
               const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
-              const int32_t* active, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+              const int32_t* active, uint8_t* hq, uint8_t* hs, const TileMap& tm, hipStream_t s) {
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem p{};
@@ -132,13 +163,14 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   p.N = I; p.K = H;
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = hq; p.h_s = hs;
-  moe::launch_gemm1_small(f, p, max_active, s);
+  if (routed_mfma(d, M, packed)) moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  else moe::launch_gemm1_small(f, p, max_active, s);
 }
 
 // GEMM2: H rows of w2 over I inputs; activation row = sorted position; output row = pair id.
 void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, const moe_mxfp4_experts* packed,
               const moe_bf16_experts* decoded, const int32_t* offsets, const int32_t* pairs, const int32_t* active,
-              uint16_t* slot, hipStream_t s) {
+              uint16_t* slot, const TileMap& tm, hipStream_t s) {
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem q{};
@@ -157,14 +189,17 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.N = H; q.K = I;
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot;
-  moe::launch_gemm2_small(f, q, max_active, s);
+  if (routed_mfma(d, M, packed)) moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  else moe::launch_gemm2_small(f, q, max_active, s);
 }
 
 void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
                    const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
-                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, hipStream_t s) {
-  do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, s);
-  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, s);
+                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, void* ws, hipStream_t s) {
+  TileMap tm;
+  if (routed_mfma(d, M, packed)) tm = make_tile_map(d, M, offsets, ws, s);
+  do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, tm, s);
+  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, tm, s);
 }
 
 void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_fp8_expert* sh,
@@ -177,13 +212,16 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
   p.N = I; p.K = H;
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = shq; p.h_s = shs;
-  moe::launch_gemm1_small(moe::W_FP8_BLOCK32, p, 1, s);
+  const TileMap none;
+  if (shared_mfma(M)) moe::launch_gemm1_mfma(moe::W_FP8_BLOCK32, p, 0, none.tile_e, none.tile_r0, s);
+  else moe::launch_gemm1_small(moe::W_FP8_BLOCK32, p, 1, s);
   GemmProblem q = p;
   q.wa = sh->w2; q.sa = sh->s2; q.wb = nullptr; q.sb = nullptr;
   q.N = H; q.K = I;
   q.act_q = shq; q.act_s = shs; q.act_by_token = 0;
   q.out = out;
-  moe::launch_gemm2_small(moe::W_FP8_BLOCK32, q, 1, s);
+  if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, s);
+  else moe::launch_gemm2_small(moe::W_FP8_BLOCK32, q, 1, s);
 }
 
 }  // namespace
@@ -246,7 +284,7 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
     h_q = at<uint8_t>(ws, L.h_q);
     h_s = at<uint8_t>(ws, L.h_s);
   }
-  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s,
+  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s, ws,
                 static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -254,7 +292,7 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
 moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
                             const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
                             const int32_t* offsets, const int32_t* pairs, const int32_t* active, uint8_t* h_q,
-                            uint8_t* h_s, void* stream) {
+                            uint8_t* h_s, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims, M));
   if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
@@ -262,21 +300,29 @@ moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q,
   if (!al(x_q, 16) || !x_s || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(h_q, 16) ||
       !h_s)
     return MOE_ERR_INVALID_ARG;
-  do_gemm1(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, h_q, h_s, static_cast<hipStream_t>(stream));
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TileMap tm;
+  if (routed_mfma(dims, M, packed)) tm = make_tile_map(dims, M, offsets, ws, s);
+  do_gemm1(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, h_q, h_s, tm, s);
   return launched();
 }
 
 moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q, const uint8_t* h_s,
                             const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
                             const int32_t* offsets, const int32_t* pairs, const int32_t* active,
-                            uint16_t* slot_out, void* stream) {
+                            uint16_t* slot_out, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims, M));
   if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
   if (!al(h_q, 16) || !h_s || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
     return MOE_ERR_INVALID_ARG;
-  do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, static_cast<hipStream_t>(stream));
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TileMap tm;
+  if (routed_mfma(dims, M, packed)) tm = make_tile_map(dims, M, offsets, ws, s);
+  do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, tm, s);
   return launched();
 }
 
@@ -332,7 +378,7 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                       at<int32_t>(ws, L.inv), active, s);
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, at<uint8_t>(ws, L.h_q),
-                at<uint8_t>(ws, L.h_s), s);
+                at<uint8_t>(ws, L.h_s), ws, s);
   uint16_t* sh_out = nullptr;
   if (shared != nullptr) {
     sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);

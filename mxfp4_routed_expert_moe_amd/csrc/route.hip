@@ -7,49 +7,52 @@
 // 2^ceil(log2(max(amax, 1e-4) / 448)) and E4M3 codes; done once per row and shared by every expert.
 //
 // Fixed fp32 orders (recorded so routing is reproducible): each logit is accumulated in fp32 as
-// strided partial sums (small M: 64 lanes x 4 interleaved FMA chains, then a butterfly; large M:
-// 32-wide chunks summed into a running total); the normalising sum adds the k weights in slot order.
+// strided partial sums (small M: per 512-wide chunk of H, 64 lanes x an 8-FMA chain, then a
+// butterfly, then the chunks added in ascending order; large M: 32-wide chunks summed into a running
+// total); the normalising sum adds the k weights in slot order.
 #include "kernels.h"
 #include "moe_device.h"
 
 namespace moe {
 
 constexpr int kSmallM = 64;
+constexpr int kChunkH = 512;   // H columns per partial logit at small M
 
-// One wave per expert; every wave handles all M <= 64 tokens so the gate row is read once.
+// Small M: one wave per (expert, 512-wide chunk of H); lane l covers 8 consecutive columns. Every
+// wave handles all M <= 64 tokens, so each gate element is read once. The wave's fp32 partial sum
+// (8 FMA chain per lane, then a butterfly over the 64 lanes) goes to part[chunk][t][e]; the select
+// kernel adds the chunks in ascending order.
 __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, const uint16_t* __restrict__ x,
                                                            const float* __restrict__ gate_w,
-                                                           float* __restrict__ logits) {
+                                                           float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int chunk = blockIdx.y;
   if (e >= E) return;
-  float acc[kSmallM];
-#pragma unroll
-  for (int t = 0; t < kSmallM; ++t) acc[t] = 0.0f;
-  const float* wrow = gate_w + (size_t)e * H;
-  for (int h = lane * 4; h < H; h += 256) {
-    const float4 w = *reinterpret_cast<const float4*>(wrow + h);
-#pragma unroll
-    for (int t = 0; t < kSmallM; ++t) {
-      if (t < M) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * H + h);
-        float a = acc[t];
-        a = __builtin_fmaf(bits_to_f32(xv.x << 16), w.x, a);
-        a = __builtin_fmaf(bits_to_f32(xv.x & 0xFFFF0000u), w.y, a);
-        a = __builtin_fmaf(bits_to_f32(xv.y << 16), w.z, a);
-        a = __builtin_fmaf(bits_to_f32(xv.y & 0xFFFF0000u), w.w, a);
-        acc[t] = a;
-      }
-    }
+  const int h = chunk * kChunkH + lane * 8;
+  const bool ok = h < H;
+  float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0;
+  if (ok) {
+    w0 = *reinterpret_cast<const float4*>(gate_w + (size_t)e * H + h);
+    w1 = *reinterpret_cast<const float4*>(gate_w + (size_t)e * H + h + 4);
   }
-#pragma unroll
-  for (int t = 0; t < kSmallM; ++t) {
-    if (t < M) {
-      float v = acc[t];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) logits[(size_t)t * E + e] = v;
+  const size_t plane = (size_t)M * E;
+  for (int t = 0; t < M; ++t) {
+    float a = 0.0f;
+    if (ok) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h);
+      a = __builtin_fmaf(bits_to_f32(xv[0] << 16), w0.x, a);
+      a = __builtin_fmaf(bits_to_f32(xv[0] & 0xFFFF0000u), w0.y, a);
+      a = __builtin_fmaf(bits_to_f32(xv[1] << 16), w0.z, a);
+      a = __builtin_fmaf(bits_to_f32(xv[1] & 0xFFFF0000u), w0.w, a);
+      a = __builtin_fmaf(bits_to_f32(xv[2] << 16), w1.x, a);
+      a = __builtin_fmaf(bits_to_f32(xv[2] & 0xFFFF0000u), w1.y, a);
+      a = __builtin_fmaf(bits_to_f32(xv[3] << 16), w1.z, a);
+      a = __builtin_fmaf(bits_to_f32(xv[3] & 0xFFFF0000u), w1.w, a);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
+    if (lane == 0) part[(size_t)chunk * plane + (size_t)t * E + e] = a;
   }
 }
 
@@ -130,7 +133,7 @@ __device__ __forceinline__ Cand better(Cand a, Cand b) {
 
 // One wave per token: scores, biased top-k, normalisation, then the QDQ of the token's row.
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
-                                                         const float* __restrict__ logits,
+                                                         int nparts, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
                                                          const uint16_t* __restrict__ x,
                                                          int32_t* __restrict__ ids, float* __restrict__ rw,
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
     const int e = lane + 64 * j;
     sc[j] = 0.0f; sel[j] = -INFINITY;
     if (e < E) {
-      const float l = logits[(size_t)t * E + e];
+      float l = logits[(size_t)t * E + e];
+      for (int c = 1; c < nparts; ++c) l = l + logits[(size_t)c * M * E + (size_t)t * E + e];
       const float sp = l > 20.0f ? l : log1pf(expf(l));
       sc[j] = sqrtf(sp);
       sel[j] = sc[j] + gate_b[e];
@@ -223,10 +227,12 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
   }
 }
 
+int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : 1; }
+
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
                           hipStream_t s) {
   if (M <= kSmallM) {
-    router_logits_small<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
+    router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
   } else {
     router_logits_tiled<<<dim3((M + 31) / 32, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
   }
@@ -235,8 +241,8 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
                               uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  router_select_qdq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, logits, gate_b, x, ids,
-                                                            rw, x_q, x_s);
+  router_select_qdq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
+                                                            logits, gate_b, x, ids, rw, x_q, x_s);
 }
 
 }  // namespace moe

@@ -140,3 +140,16 @@ def test_component_calls_refuse_before_launch(lib):
     assert lib.moe_expand_mxfp4(16, 48, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert lib.moe_expand_mxfp4(-1, 64, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_expand_mxfp4(0, 64, FAKE, FAKE, FAKE, None) == OK
+
+
+def test_workspace_never_shrinks_as_m_grows(lib):
+    """A workspace sized for max_tokens must serve every call with M <= max_tokens."""
+    f = lib.moe_workspace_bytes
+    f.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+    f.restype = ctypes.c_size_t
+    for d in (big(), Dims(8, 256, 128, 2, 1.5), Dims(256, 1024, 512, 8, 1.0)):
+        prev = 0
+        for M in list(range(0, 300)) + [1000, 4096, 8192, 8193]:
+            w = f(ctypes.byref(d), M)
+            assert w >= prev, (M, w, prev)
+            prev = w

@@ -264,3 +264,77 @@ def test_all_tokens_on_the_same_experts():
     assert np.array_equal(np.sort(res["ids"], axis=1), np.tile([3, 17, 40, 77, 90, 127], (cfg.M, 1)))
     check_routing(res["ids"], res["rw"], ref["route"], cfg)
     assert_within(res["out"], ref["out"], "forced routing")
+
+
+# ---------------------------------------------------------------------------------------------
+# the prefill-width path (block-scaled MFMA grouped GEMM): taken when M * k >= 32 * E. Layer sizes
+# the oracle computes in full, spanning several row tiles (128) per expert with ragged tails,
+# several column tiles and several K steps (128).
+MFMA_CASES = [
+    dict(M=1000, H=512, I=256, E=8, k=2),
+    dict(M=777, H=1024, I=384, E=16, k=4),
+    dict(M=300, H=256, I=128, E=8, k=2, shared=True),
+]
+
+
+@pytest.mark.parametrize("over", MFMA_CASES, ids=lambda o: "M{M}_H{H}_I{I}_E{E}_k{k}".format(**o))
+def test_prefill_path_matches_oracle_on_every_token(over):
+    cfg, inp, d = cfg_inputs(0, **over)
+    assert cfg.M * cfg.k >= 32 * cfg.E
+    res = forward(cfg, d)
+    ref = O.moe_forward(inp, cfg)
+    diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
+    if diff.size:
+        ref = O.moe_forward(inp, cfg, ids=res["ids"], rw=res["rw"])
+    mx, l2 = assert_within(res["out"], ref["out"], f"{cfg.name} {over}")
+    print(f"{over}: max-err ratio {mx:.3g}, rel-L2 {l2:.3g}")
+    if cfg.shared:
+        assert_within(res["shared_out"], ref["shared_y"], "shared expert (MFMA path)")
+
+
+def test_prefill_path_h_codes_on_oracle_routing():
+    cfg, inp, d = cfg_inputs(0, M=1000, H=512, I=256, E=8, k=2)
+    ref = O.moe_forward(inp, cfg)
+    M, k, E = cfg.M, cfg.k, cfg.E
+    dims = dims_of(cfg)
+    ws = m().workspace(dims, M)
+    ids = torch.from_numpy(ref["ids"]).cuda()
+    rw = torch.from_numpy(ref["rw"]).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pairs = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    active = torch.empty(E, dtype=torch.int32, device="cuda")
+    m().moe_permute(dims, ids, counts, offsets, pairs, None, active)
+    hq = torch.empty((M * k, cfg.I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((M * k, cfg.I // 32), dtype=torch.uint8, device="cuda")
+    m().moe_expert_gemm1(dims, dev_tensor(ref["xq"]), dev_tensor(ref["xs"]), packed_of(d), None, rw, offsets, pairs,
+                         active, hq, hs, ws)
+    slot = torch.empty((M * k, cfg.H), dtype=torch.int16, device="cuda")
+    m().moe_expert_gemm2(dims, M, hq, hs, packed_of(d), None, offsets, pairs, active, slot, ws)
+    torch.cuda.synchronize()
+    pr = pairs.cpu().numpy()
+    hq_g = np.empty_like(hq.cpu().numpy())
+    hq_g[pr] = hq.cpu().numpy()
+    hs_g = np.empty_like(hs.cpu().numpy())
+    hs_g[pr] = hs.cpu().numpy()
+    same = np.mean(hq_g.reshape(M, k, cfg.I) == ref["hq"])
+    same_s = np.mean(hs_g.reshape(M, k, -1) == ref["hs"])
+    print(f"MFMA path: h codes identical on {same:.5f}, h scales on {same_s:.5f} of elements")
+    assert same >= 0.99 and same_s >= 0.99
+    assert_within(bf16_host(slot).reshape(M, k, cfg.H), ref["slot_y"], "slot outputs (MFMA path)")
+
+
+def test_prefill_path_all_tokens_on_two_experts():
+    """Every token forced onto experts 1 and 5: 1000 rows each (8 row tiles), the other experts empty."""
+    cfg, inp, d = cfg_inputs(0, M=1000, H=512, I=256, E=8, k=2)
+    inp2 = dict(inp)
+    gb = inp["gate_b"].copy()
+    gb[[1, 5]] += np.float32(50.0)
+    inp2["gate_b"] = gb
+    d2 = dict(d)
+    d2["gate_b"] = dev_tensor(gb)
+    res = forward(cfg, d2)
+    ref = O.moe_forward(inp2, cfg)
+    assert np.array_equal(np.sort(res["ids"], axis=1), np.tile([1, 5], (cfg.M, 1)))
+    check_routing(res["ids"], res["rw"], ref["route"], cfg)
+    assert_within(res["out"], ref["out"], "forced routing (MFMA path)")
