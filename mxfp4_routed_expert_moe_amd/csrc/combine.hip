@@ -1,17 +1,18 @@
 // Fixed-order combine of the routed experts (DeepSeek-V4.1-Flash native-tensor page, section 2
 // "MoE"): y = 0 in fp32; for the token's expert ids in ascending order, y += that expert's bf16
-// output (as fp32); then y += the shared expert's bf16 output; out = bf16(y). One token per block,
-// no atomics: the order of the adds is fixed by the ids, so the result is run-to-run identical.
+// output (as fp32); then y += the shared expert's bf16 output; out = bf16(y). A block covers 512 columns
+// of one token (8 per thread); no atomics: the order of the adds is fixed by the ids, so the result is
+// run-to-run identical.
 #include "kernels.h"
 #include "moe_device.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void combine_kernel(int H, int k, const int32_t* __restrict__ ids,
-                                                      const uint16_t* __restrict__ slot_out,
-                                                      const uint16_t* __restrict__ shared_out,
-                                                      uint16_t* __restrict__ out) {
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(64) void combine_kernel(int H, int k, const int32_t* __restrict__ ids,
+                                                     const uint16_t* __restrict__ slot_out,
+                                                     const uint16_t* __restrict__ shared_out,
+                                                     uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
   // slots of this token sorted by ascending expert id (stable in slot order; k <= 8)
   int order[8], key[8];
 #pragma unroll
@@ -27,7 +28,9 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const int32_
         const int tk = key[b]; key[b] = key[b - 1]; key[b - 1] = tk;
         const int to = order[b]; order[b] = order[b - 1]; order[b - 1] = to;
       }
-  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+  {
+    const int c = blockIdx.x * 512 + threadIdx.x * 8;   // H is a multiple of 128, so c + 8 <= H or c >= H
+    if (c >= H) return;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const int32_
 
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out, const uint16_t* shared_out,
                     uint16_t* out, hipStream_t s) {
-  combine_kernel<<<dim3(M), dim3(256), 0, s>>>(H, k, ids, slot_out, shared_out, out);
+  combine_kernel<<<dim3((H + 511) / 512, M), dim3(64), 0, s>>>(H, k, ids, slot_out, shared_out, out);
 }
 
 }  // namespace moe

@@ -211,4 +211,226 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
   launch_small<false>(f, p, max_active, s);
 }
 
+
+// =================================================================================================
+// Decode-width GEMMs on the block-scaled matrix cores (MXFP4 or FP8 weights, E4M3 activations).
+//
+// The weights stream from HBM once and feed v_mfma_scale_f32_16x16x128_f8f6f4 as stored: no
+// conversion instructions. A block owns four 16-row weight fragments (GEMM1: w1 and w3 rows of the same
+// 32 output columns, so the SwiGLU pairs and the 32-column QDQ block meet in one lane; GEMM2: 64 rows of
+// w2) and the expert's activation rows as the MFMA's 16 columns. Its four waves split the inner
+// dimension into quarters and stream 16 rows x 64 bytes per load instruction, two K steps in flight; the
+// E8M0 scales of the block's 64 rows are staged once into LDS with coalesced loads (per-step scale
+// gathers would double the L1 line traffic). The four fp32 partials are added in a fixed order in LDS.
+//
+// Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E2M1 operand
+// holds K [32g, 32g + 32) of the 128-wide step (one stored 16-byte MX block); an E4M3 operand holds
+// K [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16); lane l supplies the E8M0 scale of K block g of its
+// row (the low byte of the scale operand).
+// =================================================================================================
+namespace {
+
+constexpr int kStreamU = 2;   // K steps of loads in flight per lane
+
+template <int WF>
+struct StreamA;   // one 16-row x 128-K weight fragment of a lane
+template <>
+struct StreamA<W_MXFP4> {
+  u32x4 d;
+  __device__ __forceinline__ void load(const uint8_t* row, int ks, int g) {
+    d = *reinterpret_cast<const u32x4*>(row + ks * 64 + 16 * g);
+  }
+  __device__ __forceinline__ i32x8 frag() const {
+    return i32x8{(int)d[0], (int)d[1], (int)d[2], (int)d[3], 0, 0, 0, 0};
+  }
+  static constexpr int kFmt = 4;
+};
+template <>
+struct StreamA<W_FP8_BLOCK32> {
+  u32x4 d0, d1;
+  __device__ __forceinline__ void load(const uint8_t* row, int ks, int g) {
+    d0 = *reinterpret_cast<const u32x4*>(row + ks * 128 + 16 * g);
+    d1 = *reinterpret_cast<const u32x4*>(row + ks * 128 + 64 + 16 * g);
+  }
+  __device__ __forceinline__ i32x8 frag() const {
+    return i32x8{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
+  }
+  static constexpr int kFmt = 0;
+};
+
+}  // namespace
+
+// Dynamic LDS: [64 rows][K/32] scale bytes, then the [4 waves][4 frags][4][64] fp32 partials.
+template <int WF, bool GEMM1>
+__global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  int e, row0, nrows;
+  if (p.dense) {
+    if (blockIdx.y > 0) return;
+    e = 0; row0 = 0; nrows = p.M;
+  } else {
+    e = p.active[blockIdx.y];
+    if (e < 0) return;
+    row0 = p.offsets[e];
+    nrows = p.offsets[e + 1] - row0;
+  }
+  const int K = p.K, nk = K / 128, KB = K / 32;
+  uint8_t* sc = dyn;                                                     // [64][KB]
+  float* red = reinterpret_cast<float*>(dyn + ((64 * KB + 15) & ~15));   // [4][4][4][64]
+  // block rows: GEMM1 output columns c0 .. c0 + 31 (LDS rows 0..31 = w1, 32..63 = w3); GEMM2 rows c0 .. c0 + 63
+  const int c0 = GEMM1 ? blockIdx.x * 32 : blockIdx.x * 64;
+  auto grow_of = [&](int r) { return GEMM1 ? c0 + (r & 31) : c0 + r; };
+  auto sbase_of = [&](int r) -> const uint8_t* {
+    const uint8_t* sb = (GEMM1 && r >= 32) ? p.sb : p.sa;
+    return (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
+                           : sb + (size_t)(grow_of(r) / 32) * KB;
+  };
+  const size_t wrow_bytes = (WF == W_MXFP4) ? (size_t)K / 2 : (size_t)K;
+  const uint8_t* wrow[4];
+  int lrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    lrow[f] = GEMM1 ? 32 * (f >> 1) + 16 * (f & 1) + r16 : 16 * f + r16;
+    const uint8_t* wb = static_cast<const uint8_t*>((GEMM1 && f >= 2) ? p.wb : p.wa);
+    wrow[f] = wb + (size_t)e * p.w_expert_stride + (size_t)grow_of(lrow[f]) * wrow_bytes;
+  }
+  // stage the scales: KB/4 dwords per row (KB is a multiple of 4)
+  for (int i = threadIdx.x; i < 64 * (KB / 4); i += 256) {
+    const int r = i / (KB / 4), c = i % (KB / 4);
+    *reinterpret_cast<uint32_t*>(sc + r * KB + 4 * c) = *reinterpret_cast<const uint32_t*>(sbase_of(r) + 4 * c);
+  }
+  __syncthreads();
+  const int kb = nk * wave / 4, ke = nk * (wave + 1) / 4;
+
+  for (int tg = 0; tg < nrows; tg += 16) {
+    const bool valid = tg + r16 < nrows;
+    const int pos = row0 + tg + r16;
+    int arow = 0;
+    if (valid) arow = (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
+    const uint8_t* brow = p.act_q + (size_t)arow * K;
+    const uint8_t* bsrow = p.act_s + (size_t)arow * KB;
+    f32x4 acc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks0 = kb; ks0 < ke; ks0 += kStreamU) {
+      StreamA<WF> A[kStreamU][4];
+      u32x4 b0[kStreamU], b1[kStreamU];
+      uint32_t bs[kStreamU];
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) {
+        const int ks = ks0 + u;
+        if (ks < ke) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) A[u][f].load(wrow[f], ks, g);
+          if (valid) {
+            b0[u] = *reinterpret_cast<const u32x4*>(brow + ks * 128 + 16 * g);
+            b1[u] = *reinterpret_cast<const u32x4*>(brow + ks * 128 + 64 + 16 * g);
+            bs[u] = bsrow[4 * ks + g];
+          } else {
+            b0[u] = u32x4{0u, 0u, 0u, 0u};
+            b1[u] = b0[u];
+            bs[u] = 127u;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) {
+        const int ks = ks0 + u;
+        if (ks < ke) {
+          const i32x8 B = i32x8{(int)b0[u][0], (int)b0[u][1], (int)b0[u][2], (int)b0[u][3],
+                                (int)b1[u][0], (int)b1[u][1], (int)b1[u][2], (int)b1[u][3]};
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[u][f].frag(), B, acc[f], StreamA<WF>::kFmt, 0,
+                                                                      0, (int)sc[lrow[f] * KB + 4 * ks + g], 0,
+                                                                      (int)bs[u]);
+        }
+      }
+    }
+    // fixed-order sum of the four K quarters
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((wave * 4 + f) * 4 + v) * 64 + lane] = acc[f][v];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float s = red[((0 * 4 + f) * 4 + v) * 64 + lane];
+          s = s + red[((1 * 4 + f) * 4 + v) * 64 + lane];
+          s = s + red[((2 * 4 + f) * 4 + v) * 64 + lane];
+          s = s + red[((3 * 4 + f) * 4 + v) * 64 + lane];
+          acc[f][v] = s;
+        }
+      // lane holds weight rows 4g + v of each fragment for activation row r16
+      if constexpr (GEMM1) {
+        float rwv = 1.0f;
+        if (valid && !p.dense) rwv = p.rw[p.pairs[pos]];
+        float h[2][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gv = round_bf16(acc[half][v]);
+            const float uv = round_bf16(acc[2 + half][v]);
+            h[half][v] = round_bf16(swiglu(gv, uv, rwv, !p.dense));
+            amax = fmaxf(amax, fabsf(h[half][v]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int E8 = qdq_exponent(amax);
+        const float inv = exp2_neg(E8);
+        if (valid) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
+            *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + c0 + 16 * half + 4 * g) = packed;
+          }
+          if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + c0 / 32] = uint8_t(E8 + 127);
+        }
+      } else {
+        if (valid) {
+          const int orow = p.dense ? pos : p.pairs[pos];
+          uint16_t* o = p.out + (size_t)orow * p.N + c0 + 4 * g;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[f][0])) | (uint32_t(f32_to_bf16_rne(acc[f][1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[f][2])) | (uint32_t(f32_to_bf16_rne(acc[f][3])) << 16);
+            *reinterpret_cast<u32x2*>(o + 16 * f) = u32x2{lo, hi};
+          }
+        }
+      }
+    }
+    __syncthreads();   // the partials buffer is reused by the next row group
+  }
+}
+
+size_t stream_lds_bytes(int K) { return (size_t)((64 * (K / 32) + 15) & ~15) + 4 * 4 * 4 * 64 * sizeof(float); }
+
+template <bool GEMM1>
+static void launch_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s) {
+  dim3 grid(GEMM1 ? p.N / 32 : p.N / 64, p.dense ? 1 : max_active);
+  const size_t lds = stream_lds_bytes(p.K);
+  switch (f) {
+    case W_MXFP4: expert_gemm_stream<W_MXFP4, GEMM1><<<grid, dim3(256), lds, s>>>(p); break;
+    case W_FP8_BLOCK32: expert_gemm_stream<W_FP8_BLOCK32, GEMM1><<<grid, dim3(256), lds, s>>>(p); break;
+    default: break;   // the bf16 arm uses launch_small
+  }
+}
+
+void launch_gemm1_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s) {
+  launch_stream<true>(f, p, max_active, s);
+}
+
+void launch_gemm2_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s) {
+  launch_stream<false>(f, p, max_active, s);
+}
+
 }  // namespace moe

@@ -54,6 +54,9 @@ struct GemmProblem {
 void launch_gemm1_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
 // GEMM2: y = w2 h -> bf16 rows
 void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
+// The same at decode width on the block-scaled matrix cores (MXFP4 or FP8 weights only).
+void launch_gemm1_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
+void launch_gemm2_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
 
 // ---- expert GEMMs on the block-scaled matrix cores (expert_mfma.hip) ---------------------------
 // Upper bound of the row-tile list for P (token, slot) pairs over E experts.

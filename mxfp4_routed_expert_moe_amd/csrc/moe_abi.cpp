@@ -69,6 +69,7 @@ moe_status check_dims(const moe_dims* d, int32_t M) {
   if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || !std::isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
   if (E > 256 || k > 8 || k > E) return MOE_ERR_UNSUPPORTED;
   if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H > 16384 || I > 16384) return MOE_ERR_UNSUPPORTED;   // per-block scale staging fits in LDS
   if ((int64_t)H * I > (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (M > (1 << 24) || (int64_t)M * k > (int64_t(1) << 26)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -164,6 +165,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = hq; p.h_s = hs;
   if (routed_mfma(d, M, packed)) moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  else if (packed) moe::launch_gemm1_stream(f, p, max_active, s);
   else moe::launch_gemm1_small(f, p, max_active, s);
 }
 
@@ -190,6 +192,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot;
   if (routed_mfma(d, M, packed)) moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  else if (packed) moe::launch_gemm2_stream(f, q, max_active, s);
   else moe::launch_gemm2_small(f, q, max_active, s);
 }
 
@@ -214,14 +217,14 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
   p.h_q = shq; p.h_s = shs;
   const TileMap none;
   if (shared_mfma(M)) moe::launch_gemm1_mfma(moe::W_FP8_BLOCK32, p, 0, none.tile_e, none.tile_r0, s);
-  else moe::launch_gemm1_small(moe::W_FP8_BLOCK32, p, 1, s);
+  else moe::launch_gemm1_stream(moe::W_FP8_BLOCK32, p, 1, s);
   GemmProblem q = p;
   q.wa = sh->w2; q.sa = sh->s2; q.wb = nullptr; q.sb = nullptr;
   q.N = H; q.K = I;
   q.act_q = shq; q.act_s = shs; q.act_by_token = 0;
   q.out = out;
   if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, s);
-  else moe::launch_gemm2_small(moe::W_FP8_BLOCK32, q, 1, s);
+  else moe::launch_gemm2_stream(moe::W_FP8_BLOCK32, q, 1, s);
 }
 
 }  // namespace

@@ -70,9 +70,71 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
   }
 }
 
+// Up to 1024 pairs (decode widths): one block. LDS histogram, block scan of the counts and of the
+// active flags, and the stable rank of pair p inside its expert = the number of earlier pairs with the
+// same id (one LDS sweep per thread).
+constexpr int kSmallPairs = 1024;
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(int P, int E, const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
+                                                             int32_t* __restrict__ active) {
+  __shared__ int sid[kSmallPairs];
+  __shared__ int hist[256];
+  __shared__ int scan[256];
+  __shared__ int ascan[256];
+  const int tid = threadIdx.x;
+  if (tid < 256) hist[tid] = 0;
+  int v = -1;
+  if (tid < P) v = ids[tid];
+  const bool ok = v >= 0 && v < E;
+  sid[tid] = ok ? v : -1;
+  __syncthreads();
+  if (ok) atomicAdd(&hist[v], 1);   // integer counts: order-free
+  __syncthreads();
+  if (tid < 256) {
+    scan[tid] = tid < E ? hist[tid] : 0;
+    ascan[tid] = (tid < E && hist[tid] > 0) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {   // inclusive Hillis-Steele scans
+    int a = 0, b = 0;
+    if (tid < 256 && tid >= d) {
+      a = scan[tid - d];
+      b = ascan[tid - d];
+    }
+    __syncthreads();
+    if (tid < 256) {
+      scan[tid] += a;
+      ascan[tid] += b;
+    }
+    __syncthreads();
+  }
+  const int n_active = ascan[255];
+  if (tid < E) {
+    const int c = hist[tid];
+    counts[tid] = c;
+    offsets[tid] = scan[tid] - c;
+    if (c > 0) active[ascan[tid] - 1] = tid;   // positions < n_active
+    if (tid >= n_active) active[tid] = -1;      // padding: positions >= n_active, disjoint from the above
+  }
+  if (tid == 0) offsets[E] = scan[255];
+  if (ok) {
+    int r = 0;
+    for (int q = 0; q < tid; ++q) r += (sid[q] == v) ? 1 : 0;
+    const int pos = scan[v] - hist[v] + r;
+    pairs[pos] = tid;
+    if (inv) inv[tid] = pos;
+  }
+}
+
 void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs,
                     int32_t* inv, int32_t* active, hipStream_t s) {
-  permute_kernel<<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+  if (P <= kSmallPairs)
+    permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+  else
+    permute_kernel<<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
 }
 
 }  // namespace moe

@@ -131,7 +131,8 @@ __device__ __forceinline__ Cand better(Cand a, Cand b) {
   return (a.v > b.v || (a.v == b.v && a.i < b.i)) ? a : b;
 }
 
-// One wave per token: scores, biased top-k, normalisation, then the QDQ of the token's row.
+// One block per token. Wave 0: scores, biased top-k, normalisation; all four waves: the QDQ of the
+// token's row (one 32-wide block per thread).
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
                                                          int nparts, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
                                                          int32_t* __restrict__ ids, float* __restrict__ rw,
                                                          uint8_t* __restrict__ x_q, uint8_t* __restrict__ x_s) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= M) return;
+  const int t = blockIdx.x;
+  if (threadIdx.x < 64) {
   // ---- scores and selection values: lane owns experts lane, lane + 64, ... (E <= 256)
   float sc[4], sel[4];
 #pragma unroll
@@ -148,8 +149,19 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
     const int e = lane + 64 * j;
     sc[j] = 0.0f; sel[j] = -INFINITY;
     if (e < E) {
-      float l = logits[(size_t)t * E + e];
-      for (int c = 1; c < nparts; ++c) l = l + logits[(size_t)c * M * E + (size_t)t * E + e];
+      // partial logits added in ascending chunk order; four loads in flight at a time
+      const float* lp = logits + (size_t)t * E + e;
+      const size_t plane = (size_t)M * E;
+      float l = lp[0];
+      int c = 1;
+      for (; c + 3 < nparts; c += 4) {
+        const float a0 = lp[c * plane], a1 = lp[(c + 1) * plane], a2 = lp[(c + 2) * plane], a3 = lp[(c + 3) * plane];
+        l = l + a0;
+        l = l + a1;
+        l = l + a2;
+        l = l + a3;
+      }
+      for (; c < nparts; ++c) l = l + lp[c * plane];
       const float sp = l > 20.0f ? l : log1pf(expf(l));
       sc[j] = sqrtf(sp);
       sel[j] = sc[j] + gate_b[e];
@@ -193,9 +205,10 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
       }
     }
   }
-  // ---- QDQ of the row: one 32-wide block per lane per iteration
+  }
+  // ---- QDQ of the row: one 32-wide block per thread per iteration
   const int nb = H / 32;
-  for (int b = lane; b < nb; b += 64) {
+  for (int b = threadIdx.x; b < nb; b += 256) {
     const uint16_t* src = x + (size_t)t * H + b * 32;
     u32x4 raw[4];
 #pragma unroll
@@ -241,7 +254,7 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
                               uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  router_select_qdq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
+  router_select_qdq<<<dim3(M), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
                                                             logits, gate_b, x, ids, rw, x_q, x_s);
 }
 
