@@ -13,10 +13,11 @@
 // 16; in both cases lane l supplies the E8M0 scale of K block g ([32g, 32g + 32)) of its row. The
 // result element (row 4g + v of A, row l % 16 of B) is accumulator v of lane l.
 //
-// Tiling. A block computes 128 weight rows x 128 rows of one expert (GEMM1: the same 64 output columns
-// of w1 and w3, so the SwiGLU pairs sit in one lane). Four waves in a 2 x 2 layout each own 64 weight
-// rows x 64 rows (16 MFMAs per 128-wide K step, 64 fp32 accumulators per lane). K steps of 128 are
-// staged through double-buffered LDS with padded row strides (conflict-free 128-bit reads). The rows of
+// Tiling. A block computes 256 weight rows x 128 rows of one expert (GEMM1: the same 128 output columns
+// of w1 and w3, so the SwiGLU pairs sit in one lane). Four waves in a 2 x 2 layout each own 128 weight
+// rows x 64 rows (32 MFMAs per 128-wide K step, 128 fp32 accumulators per lane: the larger wave tile
+// cuts LDS bytes per MFMA). K steps of 128 stream into a three-stage LDS ring by direct global-to-LDS
+// copies issued two stages ahead, with XOR-swizzled 16-byte chunks (conflict-free fragment reads). The rows of
 // an expert are its sorted positions offsets[e] .. offsets[e+1]; GEMM1 gathers the activation row of
 // each position's token, GEMM2 reads the QDQ'd h rows in sorted order and scatters y to the pair's slot
 // row. The (expert, row tile) of a block comes from a tile list built on the device from the expert
@@ -28,41 +29,83 @@ namespace moe {
 
 namespace {
 
-constexpr int kTileN = 128;   // weight rows per block
-constexpr int kTileM = 128;   // activation rows per block
+constexpr int kTileM = 128;   // activation rows per block (weight rows per block: the TN template argument)
 constexpr int kStepK = 128;   // K per stage (one MFMA K)
-constexpr int kActStride = kStepK + 16;              // E4M3 activation row in LDS (bytes)
-constexpr int kFmtFp8 = 0, kFmtFp4 = 4;              // operand formats of the scaled MFMA
+constexpr int kStages = 3;    // LDS ring depth: stage s + 2 is in flight while stage s is computed
+constexpr int kFmtFp8 = 0, kFmtFp4 = 4;   // operand formats of the scaled MFMA
 
 template <int WF>
 struct WTraits;
 template <>
 struct WTraits<W_MXFP4> {
-  static constexpr int kRowBytes = kStepK / 2;       // packed bytes of one weight row per stage
-  static constexpr int kStride = kRowBytes + 16;
+  static constexpr int kRowBytes = kStepK / 2;   // packed bytes of one weight row per stage
   static constexpr int kFmt = kFmtFp4;
 };
 template <>
 struct WTraits<W_FP8_BLOCK32> {
   static constexpr int kRowBytes = kStepK;
-  static constexpr int kStride = kRowBytes + 16;
   static constexpr int kFmt = kFmtFp8;
 };
 
+// XOR swizzle of the 16-byte chunks of an LDS row: physical chunk = logical chunk ^ key(row). The keys
+// make the 16 rows of an MFMA fragment read distinct banks whether ds_read_b128 serves 8 or 16 lanes
+// per cycle (checked exhaustively for both).
+template <int RowBytes>
+__device__ __forceinline__ int chunk_key(int r) {
+  if constexpr (RowBytes == 64) return (r ^ (r >> 2)) & 3;
+  else return ((r >> 1) ^ (4 * (r & 1))) & 7;
+}
+
+// One ring stage: weight rows, activation rows, and the E8M0 bytes of the stage's 4 K blocks per row.
+template <int WF, int TN>
+struct Stage {
+  uint8_t w[TN * WTraits<WF>::kRowBytes];
+  uint8_t a[kTileM * kStepK];
+  uint8_t ws[TN * 4];
+  uint8_t as[kTileM * 4];
+};
+
+// Asynchronous global -> LDS copy of 16 (or 4) bytes per lane: lane i of the wave writes at lds + i * bytes.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_wave) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (__attribute__((address_space(3))) void*)lds_wave, 16,
+                                   0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (__attribute__((address_space(3))) void*)lds_wave, 4,
+                                   0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding (older ones have landed, LDS
+// DMA included), finish this wave's LDS reads, then meet the other waves. __syncthreads() would wait
+// for every outstanding load and drain the ring.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 28) asm volatile("s_waitcnt vmcnt(28) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0 || N == 8 || N == 16 || N == 10 || N == 14 || N == 20 || N == 28, "vmcnt immediate");
+}
+
+// Fragments of one stage held in registers (double-buffered across stages).
 template <int WF>
-struct Smem {
-  uint8_t w[2][kTileN][WTraits<WF>::kStride];
-  uint8_t a[2][kTileM][kActStride];
-  uint8_t ws[2][kTileN][4];   // E8M0 of the 4 K blocks of a stage, per weight row
-  uint8_t as[2][kTileM][4];   // per activation row
+struct Frags {
+  u32x4 a0[8], a1[8];   // A fragment bytes (a1: second 16 bytes, E4M3 weights only)
+  u32x4 b0[4], b1[4];
+  int as[8], bs[4];
 };
 
 }  // namespace
 
 // Row-tile list of the grouped GEMMs: for every expert with rows, ceil(count / kTileM) tiles in
-// ascending expert order. tile_e[y] = expert (-1 past the end), tile_r0[y] = first sorted position.
+// ascending expert order. tile_e[y] = expert (-1 past the end), tile_r0[y] = first sorted position;
+// info[0] = number of tiles, info[1 + e] = first tile of expert e, info[1 + E + e] = its tile count.
 __global__ __launch_bounds__(256) void tile_map_kernel(int E, int max_tiles, const int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r0) {
+                                                       int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r0,
+                                                       int32_t* __restrict__ info) {
   __shared__ int scan[256];
   const int e = threadIdx.x;
   int nt = 0, r0 = 0;
@@ -84,179 +127,221 @@ __global__ __launch_bounds__(256) void tile_map_kernel(int E, int max_tiles, con
     tile_r0[first + i] = r0 + i * kTileM;
   }
   for (int y = total + e; y < max_tiles; y += 256) tile_e[y] = -1;
+  if (e < E) {
+    info[1 + e] = first;
+    info[1 + E + e] = nt;
+  }
+  if (e == 0) info[0] = total;
 }
 
-template <int WF, bool GEMM1>
-__global__ __launch_bounds__(256, 2) void expert_gemm_mfma(GemmProblem p, const int32_t* __restrict__ tile_e,
-                                                           const int32_t* __restrict__ tile_r0) {
+// DMA instructions per wave per stage (TN / 64 waves): weights, 64 rows per wave (MXFP4: 4 of 16 rows x
+// 64 B; FP8: 8 of 8 rows x 128 B), activations (128 rows over the waves, 8 rows x 128 B per instruction),
+// weight scales (1 of 64 rows x 4 B), activation scales (1 of 128 / waves rows x 4 B).
+template <int WF, int TN>
+constexpr int loads_per_stage() { return (WF == W_MXFP4 ? 4 : 8) + 16 / (TN / 64) + 1 + 1; }
+
+// Work order. The grid is one-dimensional: cols x (row tiles) blocks. Workgroups are dealt to the 8 XCDs
+// round-robin (block L runs on XCD L % 8), and each XCD has its own L2. Block L is remapped to work item
+// w so that every XCD gets one contiguous range of the work list, and the list runs expert by expert,
+// column tile by column tile, row tile by row tile: the blocks an XCD runs together share a weight tile
+// and the expert's activation rows stay in that XCD's L2.
+template <int WF, bool GEMM1, int TN>
+__global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const int32_t* __restrict__ tile_e,
+                                                           const int32_t* __restrict__ tile_r0,
+                                                           const int32_t* __restrict__ info) {
   using T = WTraits<WF>;
-  __shared__ Smem<WF> sm;
+  constexpr int kRB = T::kRowBytes, kCh = kRB / 16;
+  constexpr int NW = TN / 64;                          // waves (each 128 weight rows x 64 activation rows)
+  constexpr int kWInstr = 64 * kRB / 1024;             // weight DMA per wave per stage (4 or 8)
+  constexpr int kWRows = 1024 / kRB;                   // rows per instruction (16 or 8)
+  constexpr int kAInstr = 16 / NW;                     // activation DMA per wave per stage
+  constexpr int kARows = kTileM / NW;                  // activation rows per wave
+  constexpr int LPS = loads_per_stage<WF, TN>();
+  __shared__ __align__(16) Stage<WF, TN> ring[kStages];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % (NW / 2), wm = wave / (NW / 2);
 
+  const int C = GEMM1 ? p.N / (TN / 2) : (p.N + TN - 1) / TN;               // column tiles
+  const int RT = p.dense ? (p.M + kTileM - 1) / kTileM : info[0];           // row tiles
+  const int W = RT * C;
+  const int L = blockIdx.x;
+  if (L >= W) return;
+  int w = L / 8;
+  for (int i = 0; i < L % 8; ++i) w += (W - i + 7) / 8;   // blocks of the XCDs before this one
+  int first, nt;
+  if (p.dense) {
+    first = 0;
+    nt = RT;
+  } else {
+    const int ew = tile_e[w / C];
+    first = info[1 + ew];
+    nt = info[1 + p.num_experts + ew];
+  }
+  const int local = w - first * C;
+  const int cx = local / nt, ty = first + local % nt;
   int e, row0, nrows;
   if (p.dense) {
     e = 0;
-    row0 = blockIdx.y * kTileM;
+    row0 = ty * kTileM;
     nrows = min(kTileM, p.M - row0);
-    if (nrows <= 0) return;
   } else {
-    e = tile_e[blockIdx.y];
-    if (e < 0) return;
-    row0 = tile_r0[blockIdx.y];
+    e = tile_e[ty];
+    row0 = tile_r0[ty];
     nrows = min(kTileM, p.offsets[e + 1] - row0);
   }
-  const int K = p.K;
+  const int K = p.K, KB = K / 32;
   const int nk = K / kStepK;
-  // weight rows of this block: GEMM1 rows 0..63 = w1 rows n0h..n0h+63, rows 64..127 = w3 rows n0h..;
-  // GEMM2 rows 0..127 = w2 rows n0..n0+127
-  const int n0 = blockIdx.x * (GEMM1 ? kTileN / 2 : kTileN);
+  // weight rows of this block: GEMM1 LDS rows [0, TN/2) = w1 rows n0.., [TN/2, TN) = the same rows of w3;
+  // GEMM2 LDS rows [0, TN) = w2 rows n0.. (rows past N repeat row N-1 and are never stored)
+  const int n0 = cx * (GEMM1 ? TN / 2 : TN);
+  const size_t wrow_bytes = (WF == W_MXFP4) ? (size_t)K / 2 : (size_t)K;
+  auto grow_of = [&](int r) { return GEMM1 ? n0 + (r % (TN / 2)) : min(n0 + r, p.N - 1); };
 
-  // ---- per-thread global load assignments ----------------------------------------------------
-  // weights: kTileN rows x kRowBytes per stage in 16-byte chunks
-  constexpr int kWChunks = T::kRowBytes / 16;                      // 4 (FP4) or 8 (FP8) per row
-  constexpr int kWLoads = kTileN * kWChunks / 256;                 // 2 or 4 per thread
-  const uint8_t* wsrc[kWLoads];
-  int wdst_row[kWLoads], wdst_col[kWLoads];
+  // ---- per-lane DMA sources (the stage offset is added per stage) ------------------------------
+  const uint8_t* wsrc[kWInstr];
 #pragma unroll
-  for (int i = 0; i < kWLoads; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / kWChunks, ch = c % kWChunks;
-    int grow;
-    const uint8_t* base;
-    if (GEMM1) {
-      grow = n0 + (r & 63);
-      base = static_cast<const uint8_t*>(r < 64 ? p.wa : p.wb);
-    } else {
-      grow = n0 + r;
-      base = static_cast<const uint8_t*>(p.wa);
-    }
-    const size_t row_bytes = (WF == W_MXFP4) ? (size_t)K / 2 : (size_t)K;
-    wsrc[i] = base + (size_t)e * p.w_expert_stride + (size_t)grow * row_bytes + ch * 16;
-    wdst_row[i] = r;
-    wdst_col[i] = ch * 16;
+  for (int i = 0; i < kWInstr; ++i) {
+    const int r = wave * 64 + i * kWRows + lane / kCh;             // LDS weight row
+    const int gc = (lane % kCh) ^ chunk_key<kRB>(r);               // physical chunk lane%kCh holds logical gc
+    const uint8_t* base = static_cast<const uint8_t*>((GEMM1 && r >= TN / 2) ? p.wb : p.wa);
+    wsrc[i] = base + (size_t)e * p.w_expert_stride + (size_t)grow_of(r) * wrow_bytes + gc * 16;
   }
-  // weight scales: one dword (4 K blocks) per weight row, threads 0..127
-  const uint8_t* wssrc = nullptr;
-  if (tid < kTileN) {
-    const int r = tid;
-    int grow;
-    const uint8_t* base;
-    if (GEMM1) {
-      grow = n0 + (r & 63);
-      base = r < 64 ? p.sa : p.sb;
-    } else {
-      grow = n0 + r;
-      base = p.sa;
-    }
-    if (WF == W_MXFP4) wssrc = base + (size_t)e * p.s_expert_stride + (size_t)grow * (K / 32);
-    else wssrc = base + (size_t)(grow / 32) * (K / 32);
-  }
-  // activations: kTileM rows x 128 bytes per stage = 8 chunks per row, 4 per thread
-  const uint8_t* asrc[4];
-  bool aval[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i, ch = tid & 7;
-    aval[i] = r < nrows;
-    int arow = 0;
-    if (aval[i]) {
-      const int pos = row0 + r;
-      arow = (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
-    }
-    asrc[i] = p.act_q + (size_t)arow * K + ch * 16;
-  }
-  const uint8_t* assrc = nullptr;   // activation scales: threads 128..255, one dword per row
-  bool asval = false;
-  if (tid >= 128) {
-    const int r = tid - 128;
-    asval = r < nrows;
-    int arow = 0;
-    if (asval) {
-      const int pos = row0 + r;
-      arow = (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
-    }
-    assrc = p.act_s + (size_t)arow * (K / 32);
-  }
-
-  u32x4 wreg[kWLoads], areg[4];
-  uint32_t sreg = 0;
-  auto gload = [&](int ks) {
-    const int kb = ks * kStepK;
-#pragma unroll
-    for (int i = 0; i < kWLoads; ++i)
-      wreg[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + (WF == W_MXFP4 ? kb / 2 : kb));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      areg[i] = aval[i] ? *reinterpret_cast<const u32x4*>(asrc[i] + kb) : u32x4{0u, 0u, 0u, 0u};
-    if (tid < kTileN) sreg = *reinterpret_cast<const uint32_t*>(wssrc + kb / 32);
-    else sreg = asval ? *reinterpret_cast<const uint32_t*>(assrc + kb / 32) : 0x7F7F7F7Fu;
+  auto act_row = [&](int t) {   // activation row of LDS row t (rows past the tile repeat row 0)
+    const int pos = row0 + (t < nrows ? t : 0);
+    return (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
   };
-  auto lstore = [&](int buf) {
+  const uint8_t* asrc[kAInstr];
 #pragma unroll
-    for (int i = 0; i < kWLoads; ++i)
-      *reinterpret_cast<u32x4*>(&sm.w[buf][wdst_row[i]][wdst_col[i]]) = wreg[i];
+  for (int i = 0; i < kAInstr; ++i) {
+    const int t = wave * kARows + i * 8 + lane / 8;
+    const int gc = (lane % 8) ^ chunk_key<kStepK>(t);
+    asrc[i] = p.act_q + (size_t)act_row(t) * K + gc * 16;
+  }
+  const uint8_t* wssrc;
+  {
+    const int r = wave * 64 + lane;
+    const uint8_t* sb = (GEMM1 && r >= TN / 2) ? p.sb : p.sa;
+    wssrc = (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
+                            : sb + (size_t)(grow_of(r) / 32) * KB;
+  }
+  const uint8_t* assrc = p.act_s + (size_t)act_row(wave * kARows + (lane % kARows)) * KB;
+  auto issue = [&](int s) {
+    Stage<WF, TN>& st = ring[s % kStages];
+    const int k0 = s * kStepK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sm.a[buf][(tid >> 3) + 32 * i][(tid & 7) * 16]) = areg[i];
-    if (tid < kTileN) *reinterpret_cast<uint32_t*>(&sm.ws[buf][tid][0]) = sreg;
-    else *reinterpret_cast<uint32_t*>(&sm.as[buf][tid - 128][0]) = sreg;
+    for (int i = 0; i < kWInstr; ++i)
+      dma16(wsrc[i] + (WF == W_MXFP4 ? k0 / 2 : k0), &st.w[(wave * 64 + i * kWRows) * kRB]);
+#pragma unroll
+    for (int i = 0; i < kAInstr; ++i) dma16(asrc[i] + k0, &st.a[(wave * kARows + i * 8) * kStepK]);
+    dma4(wssrc + k0 / 32, &st.ws[wave * 64 * 4]);
+    if (lane < kARows) dma4(assrc + k0 / 32, &st.as[wave * kARows * 4]);
   };
 
-  // ---- main loop -------------------------------------------------------------------------------
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // LDS rows of this wave's four A fragments
-  int arow_l[4];
+  // LDS rows of this wave's eight A fragments (weight rows) and four B fragments (activation rows)
+  int arow_l[8], brow_l[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) arow_l[a] = GEMM1 ? (64 * (a >> 1) + 32 * wn + 16 * (a & 1)) : (64 * wn + 16 * a);
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    i32x8 Af[4], Bf[4];
-    int asc[4], bsc[4];
+  for (int a = 0; a < 8; ++a)
+    arow_l[a] = (GEMM1 ? ((TN / 2) * (a >> 2) + 64 * wn + 16 * (a & 3)) : (128 * wn + 16 * a)) + r16;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const uint8_t* src = &sm.w[buf][arow_l[a] + r16][0];
-      if constexpr (WF == W_MXFP4) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * g);
-        Af[a] = i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-      } else {
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + 16 * g);
-        const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
-        Af[a] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
-      }
-      asc[a] = sm.ws[buf][arow_l[a] + r16][g];
-    }
+  for (int b = 0; b < 4; ++b) brow_l[b] = 64 * wm + 16 * b + r16;
+
+  auto read_frags = [&](Frags<WF>& F, int s) {
+    const Stage<WF, TN>& st = ring[s % kStages];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const uint8_t* src = &sm.a[buf][64 * wm + 16 * b + r16][0];
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + 16 * g);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
-      Bf[b] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3], (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
-      bsc[b] = sm.as[buf][64 * wm + 16 * b + r16][g];
+      const int t = brow_l[b];
+      const int key = chunk_key<kStepK>(t);
+      F.b0[b] = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * (g ^ key)]);
+      F.b1[b] = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * ((4 + g) ^ key)]);
+      F.bs[b] = st.as[t * 4 + g];
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a) {
+      const int r = arow_l[a];
+      const int key = chunk_key<kRB>(r);
+      F.a0[a] = *reinterpret_cast<const u32x4*>(&st.w[r * kRB + 16 * (g ^ key)]);
+      if constexpr (WF == W_FP8_BLOCK32) F.a1[a] = *reinterpret_cast<const u32x4*>(&st.w[r * kRB + 16 * ((4 + g) ^ key)]);
+      F.as[a] = st.ws[r * 4 + g];
+    }
+  };
+  auto mfmas = [&](const Frags<WF>& F) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af[a], Bf[b], acc[a][b], T::kFmt, kFmtFp8, 0,
-                                                                     asc[a], 0, bsc[b]);
-    if (ks + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    for (int a = 0; a < 8; ++a) {
+      i32x8 Af;
+      if constexpr (WF == W_MXFP4)
+        Af = i32x8{(int)F.a0[a][0], (int)F.a0[a][1], (int)F.a0[a][2], (int)F.a0[a][3], 0, 0, 0, 0};
+      else
+        Af = i32x8{(int)F.a0[a][0], (int)F.a0[a][1], (int)F.a0[a][2], (int)F.a0[a][3],
+                   (int)F.a1[a][0], (int)F.a1[a][1], (int)F.a1[a][2], (int)F.a1[a][3]};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const i32x8 Bf = i32x8{(int)F.b0[b][0], (int)F.b0[b][1], (int)F.b0[b][2], (int)F.b0[b][3],
+                               (int)F.b1[b][0], (int)F.b1[b][1], (int)F.b1[b][2], (int)F.b1[b][3]};
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[a][b], T::kFmt, kFmtFp8, 0, F.as[a],
+                                                                     0, F.bs[b]);
+      }
+    }
+  };
+  // one pipelined step: stage s + 1 has landed; refill the slot of stage s; MFMAs of stage s (registers
+  // `cur`) interleaved with the LDS reads of stage s + 1 (registers `nxt`)
+  auto step = [&](Frags<WF>& cur, Frags<WF>& nxt, int s) {
+    if (s + 2 < nk) ring_barrier<LPS>();
+    else ring_barrier<0>();
+    if (s + 3 < nk) issue(s + 3);
+    mfmas(cur);
+    read_frags(nxt, s + 1);
+    // scheduling: one LDS read after each MFMA (the reads do not depend on the MFMAs)
+#pragma unroll
+    for (int i = 0; i < (WF == W_MXFP4 ? 28 : 32); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  if constexpr (NW == 4) {
+    // one wave per SIMD: fragments double-buffered in registers, LDS reads of stage s + 1 interleaved
+    // with the MFMAs of stage s
+    Frags<WF> F0, F1;
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 2) issue(2);
+    if (nk > 2) ring_barrier<2 * LPS>();   // stage 0 landed (stages 1, 2 in flight)
+    else if (nk > 1) ring_barrier<LPS>();
+    else ring_barrier<0>();
+    read_frags(F0, 0);
+    int s = 0;
+    for (; s + 2 < nk; s += 2) {   // pairs of steps keep the two register sets static
+      step(F0, F1, s);
+      step(F1, F0, s + 1);
+    }
+    if (s + 1 < nk) {
+      step(F0, F1, s);
+      mfmas(F1);
+    } else {
+      mfmas(F0);
+    }
+  } else {
+    // two waves per SIMD cover each other's LDS latency: one fragment set (fits 256 registers)
+    Frags<WF> F;
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) ring_barrier<LPS>();   // stage s landed (stage s + 1 may still be in flight)
+      else ring_barrier<0>();
+      if (s + 2 < nk) issue(s + 2);           // into the slot computed at s - 1: every wave is past it
+      read_frags(F, s);
+      mfmas(F);
+    }
   }
 
-  // ---- epilogue: lane holds weight rows 4g..4g+3 of each A fragment for row (token) r16 of each B
-  // fragment ----------------------------------------------------------------------------------------
+  // ---- epilogue: lane holds weight rows 4g..4g+3 of each A fragment for activation row r16 of each B
+  // fragment -------------------------------------------------------------------------------------------
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int tt = 64 * wm + 16 * b + r16;
@@ -265,39 +350,42 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_mfma(GemmProblem p, const 
     if constexpr (GEMM1) {
       float rwv = 1.0f;
       if (valid && !p.dense) rwv = p.rw[p.pairs[pos]];
-      float h[2][4];
-      float amax = 0.0f;
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int qb = 0; qb < 2; ++qb) {   // two 32-column QDQ blocks: fragments (2qb, 2qb+1) of w1 with those of w3
+        float h[2][4];
+        float amax = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float gv = round_bf16(acc[half][b][v]);
-          const float uv = round_bf16(acc[2 + half][b][v]);
-          h[half][v] = round_bf16(swiglu(gv, uv, rwv, !p.dense));
-          amax = fmaxf(amax, fabsf(h[half][v]));
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gv = round_bf16(acc[2 * qb + half][b][v]);
+            const float uv = round_bf16(acc[4 + 2 * qb + half][b][v]);
+            h[half][v] = round_bf16(swiglu(gv, uv, rwv, !p.dense));
+            amax = fmaxf(amax, fabsf(h[half][v]));
+          }
+        // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int E8 = qdq_exponent(amax);
+        const float inv = exp2_neg(E8);
+        if (valid) {
+          const int col0 = n0 + 64 * wn + 32 * qb;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
+            *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + col0 + 16 * half + 4 * g) = packed;
+          }
+          if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + col0 / 32] = uint8_t(E8 + 127);
         }
-      // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      const int E8 = qdq_exponent(amax);
-      const float inv = exp2_neg(E8);
-      if (valid) {
-        const int col0 = n0 + 32 * wn;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t packed = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
-          *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + col0 + 16 * half + 4 * g) = packed;
-        }
-        if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + col0 / 32] = uint8_t(E8 + 127);
       }
     } else {
-      if (valid) {
+      if (valid && n0 + 128 * wn < p.N) {
         const int orow = p.dense ? pos : p.pairs[pos];
-        uint16_t* o = p.out + (size_t)orow * p.N + n0 + 64 * wn + 4 * g;
+        uint16_t* o = p.out + (size_t)orow * p.N + n0 + 128 * wn + 4 * g;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 8; ++a) {
           const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[a][b][0])) | (uint32_t(f32_to_bf16_rne(acc[a][b][1])) << 16);
           const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[a][b][2])) | (uint32_t(f32_to_bf16_rne(acc[a][b][3])) << 16);
           *reinterpret_cast<u32x2*>(o + 16 * a) = u32x2{lo, hi};
@@ -309,31 +397,42 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_mfma(GemmProblem p, const 
 
 int mfma_max_tiles(int P, int E) { return (P + kTileM - 1) / kTileM + (P < E ? P : E); }
 
-void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0, hipStream_t s) {
-  tile_map_kernel<<<dim3(1), dim3(256), 0, s>>>(E, max_tiles, offsets, tile_e, tile_r0);
+void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0, int32_t* info,
+                     hipStream_t s) {
+  tile_map_kernel<<<dim3(1), dim3(256), 0, s>>>(E, max_tiles, offsets, tile_e, tile_r0, info);
 }
 
+template <int WF, bool GEMM1, int TN>
+static void launch_mfma_tn(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
+                           const int32_t* info, hipStream_t s) {
+  const int cols = GEMM1 ? p.N / (TN / 2) : (p.N + TN - 1) / TN;
+  const int rows = p.dense ? (p.M + kTileM - 1) / kTileM : max_tiles;
+  expert_gemm_mfma<WF, GEMM1, TN><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
+}
+
+// MXFP4 weights: 512 weight rows per block (8 waves) when the columns divide evenly, else 256; FP8 weights
+// (twice the bytes per row): 256.
 template <bool GEMM1>
 static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
-                        const int32_t* tile_r0, hipStream_t s) {
-  const int cols = GEMM1 ? p.N / (kTileN / 2) : p.N / kTileN;
-  const int rows = p.dense ? (p.M + kTileM - 1) / kTileM : max_tiles;
-  dim3 grid(cols, rows);
+                        const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
   switch (f) {
-    case W_MXFP4: expert_gemm_mfma<W_MXFP4, GEMM1><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0); break;
-    case W_FP8_BLOCK32: expert_gemm_mfma<W_FP8_BLOCK32, GEMM1><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0); break;
+    case W_MXFP4:
+      if (!GEMM1 || p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 512>(p, max_tiles, tile_e, tile_r0, info, s);
+      else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
+      break;
+    case W_FP8_BLOCK32: launch_mfma_tn<W_FP8_BLOCK32, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s); break;
     default: break;   // the bf16 arm has no block-scaled form; the caller never asks for it here
   }
 }
 
 void launch_gemm1_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
-                       const int32_t* tile_r0, hipStream_t s) {
-  launch_mfma<true>(f, p, max_tiles, tile_e, tile_r0, s);
+                       const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
+  launch_mfma<true>(f, p, max_tiles, tile_e, tile_r0, info, s);
 }
 
 void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
-                       const int32_t* tile_r0, hipStream_t s) {
-  launch_mfma<false>(f, p, max_tiles, tile_e, tile_r0, s);
+                       const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
+  launch_mfma<false>(f, p, max_tiles, tile_e, tile_r0, info, s);
 }
 
 }  // namespace moe

@@ -41,6 +41,7 @@ struct GemmProblem {
   const uint8_t* act_q; const uint8_t* act_s;
   // routing: dense = one pseudo-expert over rows 0..M-1 in order (shared expert)
   int dense; int M; int k;
+  int num_experts;             // E (routed problems)
   const int32_t* offsets;      // [E + 1]
   const int32_t* pairs;        // [M * k]: pair id t * k + j at each sorted position
   const int32_t* active;       // [E]: active expert ids (ascending, -1 padded)
@@ -61,14 +62,15 @@ void launch_gemm2_stream(WeightFormat f, const GemmProblem& p, int max_active, h
 // ---- expert GEMMs on the block-scaled matrix cores (expert_mfma.hip) ---------------------------
 // Upper bound of the row-tile list for P (token, slot) pairs over E experts.
 int mfma_max_tiles(int P, int E);
-// Row-tile list from the expert offsets: tile_e [max_tiles] (-1 past the end), tile_r0 [max_tiles].
-void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0,
+// Row-tile list from the expert offsets: tile_e [max_tiles] (-1 past the end), tile_r0 [max_tiles],
+// info [1 + 2E] (tile count, first tile and tile count of each expert).
+void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0, int32_t* info,
                      hipStream_t s);
 // Same problems as the *_small launchers (MXFP4 or FP8 weights only); routed problems take the tile list.
 void launch_gemm1_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
-                       const int32_t* tile_r0, hipStream_t s);
+                       const int32_t* tile_r0, const int32_t* info, hipStream_t s);
 void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
-                       const int32_t* tile_r0, hipStream_t s);
+                       const int32_t* tile_r0, const int32_t* info, hipStream_t s);
 
 // ---- combine (combine.hip) -----------------------------------------------------------------
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,

@@ -15,8 +15,8 @@ namespace {
 using moe::GemmProblem;
 
 struct WsLayout {
-  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, h_q, h_s, slot, sh_q, sh_s,
-      sh_out;
+  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
+      sh_q, sh_s, sh_out;
   size_t total;
 };
 
@@ -46,6 +46,7 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.active = take(E * 4);
   L.tile_e = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
   L.tile_r0 = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
+  L.tile_info = take((1 + 2 * E) * 4);
   L.h_q = take(m * k * I);
   L.h_s = take(m * k * I / 32);
   L.slot = take(m * k * H * 2);
@@ -119,6 +120,7 @@ struct TileMap {
   int max_tiles = 0;
   const int32_t* tile_e = nullptr;
   const int32_t* tile_r0 = nullptr;
+  const int32_t* info = nullptr;
 };
 
 TileMap make_tile_map(const moe_dims* d, int M, const int32_t* offsets, void* ws, hipStream_t s) {
@@ -127,9 +129,11 @@ TileMap make_tile_map(const moe_dims* d, int M, const int32_t* offsets, void* ws
   t.max_tiles = moe::mfma_max_tiles(M * d->top_k, d->num_experts);
   int32_t* te = at<int32_t>(ws, L.tile_e);
   int32_t* tr = at<int32_t>(ws, L.tile_r0);
-  moe::launch_tile_map(d->num_experts, t.max_tiles, offsets, te, tr, s);
+  int32_t* ti = at<int32_t>(ws, L.tile_info);
+  moe::launch_tile_map(d->num_experts, t.max_tiles, offsets, te, tr, ti, s);
   t.tile_e = te;
   t.tile_r0 = tr;
+  t.info = ti;
   return t;
 }
 void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, const float* gb, int32_t* ids,
@@ -149,7 +153,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem p{};
-  p.dense = 0; p.M = M; p.k = k;
+  p.dense = 0; p.M = M; p.k = k; p.num_experts = E;
   p.offsets = offsets; p.pairs = pairs; p.active = active; p.rw = rw;
   moe::WeightFormat f;
   if (packed) {
@@ -164,7 +168,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   p.N = I; p.K = H;
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = hq; p.h_s = hs;
-  if (routed_mfma(d, M, packed)) moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  if (routed_mfma(d, M, packed)) moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   else if (packed) moe::launch_gemm1_stream(f, p, max_active, s);
   else moe::launch_gemm1_small(f, p, max_active, s);
 }
@@ -176,7 +180,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem q{};
-  q.dense = 0; q.M = M; q.k = k;
+  q.dense = 0; q.M = M; q.k = k; q.num_experts = E;
   q.offsets = offsets; q.pairs = pairs; q.active = active; q.rw = nullptr;
   moe::WeightFormat f;
   if (packed) {
@@ -191,7 +195,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.N = H; q.K = I;
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot;
-  if (routed_mfma(d, M, packed)) moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, s);
+  if (routed_mfma(d, M, packed)) moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   else if (packed) moe::launch_gemm2_stream(f, q, max_active, s);
   else moe::launch_gemm2_small(f, q, max_active, s);
 }
@@ -209,21 +213,21 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
                uint8_t* shq, uint8_t* shs, uint16_t* out, hipStream_t s) {
   const int H = d->hidden, I = d->inter;
   GemmProblem p{};
-  p.dense = 1; p.M = M; p.k = 1;
+  p.dense = 1; p.M = M; p.k = 1; p.num_experts = 1;
   p.wa = sh->w1; p.sa = sh->s1; p.wb = sh->w3; p.sb = sh->s3;
   p.w_expert_stride = 0; p.s_expert_stride = 0;
   p.N = I; p.K = H;
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = shq; p.h_s = shs;
   const TileMap none;
-  if (shared_mfma(M)) moe::launch_gemm1_mfma(moe::W_FP8_BLOCK32, p, 0, none.tile_e, none.tile_r0, s);
+  if (shared_mfma(M)) moe::launch_gemm1_mfma(moe::W_FP8_BLOCK32, p, 0, none.tile_e, none.tile_r0, none.info, s);
   else moe::launch_gemm1_stream(moe::W_FP8_BLOCK32, p, 1, s);
   GemmProblem q = p;
   q.wa = sh->w2; q.sa = sh->s2; q.wb = nullptr; q.sb = nullptr;
   q.N = H; q.K = I;
   q.act_q = shq; q.act_s = shs; q.act_by_token = 0;
   q.out = out;
-  if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, s);
+  if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, none.info, s);
   else moe::launch_gemm2_stream(moe::W_FP8_BLOCK32, q, 1, s);
 }
 
