@@ -34,7 +34,7 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   // router logits: partial planes at small M; sized so the total never shrinks as M grows (a
   // workspace sized for max_tokens serves every M <= max_tokens)
   const size_t small_rows = std::min<size_t>(m, 64) * (size_t)moe::router_logit_parts(1, (int)H);
-  L.logits = take(std::max(m, small_rows) * E * 4);
+  L.logits = take(std::max(m * (size_t)moe::router_logit_parts(1 << 20, (int)H), small_rows) * E * 4);
   L.ids = take(m * k * 4);
   L.rw = take(m * k * 4);
   L.x_q = take(m * H);

@@ -8,8 +8,9 @@
 //
 // Fixed fp32 orders (recorded so routing is reproducible): each logit is accumulated in fp32 as
 // strided partial sums (small M: per 512-wide chunk of H, 64 lanes x an 8-FMA chain, then a
-// butterfly, then the chunks added in ascending order; large M: 32-wide chunks summed into a running
-// total); the normalising sum adds the k weights in slot order.
+// butterfly, then the chunks added in ascending order; large M: per quarter of H, 32-wide FMA chains
+// summed into a running total, then the quarters added in ascending order); the normalising sum adds
+// the k weights in slot order.
 #include "kernels.h"
 #include "moe_device.h"
 
@@ -56,71 +57,84 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
   }
 }
 
-// Tiled fp32 logits for larger M: a block computes 32 tokens x 128 experts, H in chunks of 32.
+// Larger M: a block computes 64 tokens x 128 experts over one quarter of H (the quarters are added in
+// ascending order by the select kernel). Per 32-column chunk, x (transposed, fp32) and the gate tile
+// (transposed) sit in LDS; thread (tg, eg) owns tokens 8 tg .. 8 tg + 7 and experts 4 eg .. 4 eg + 3,
+// reads two float4 of x and one float4 of the gate per column, and runs 32 FMA chains. Each chunk's
+// 32-term chain is added to a running fp32 total.
+constexpr int kLargeParts = 4;
+
 __global__ __launch_bounds__(256) void router_logits_tiled(int M, int H, int E, const uint16_t* __restrict__ x,
                                                            const float* __restrict__ gate_w,
-                                                           float* __restrict__ logits) {
-  __shared__ float xs[32][33];
-  __shared__ float ws[128][33];
+                                                           float* __restrict__ part) {
+  __shared__ __align__(16) float xs[32][64];
+  __shared__ __align__(16) float ws[32][128];
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 128;
-  const int tt = tid >> 5, te = tid & 31;
-  float acc[4][4];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.z * 128;
+  const int hq = H / kLargeParts, hbeg = blockIdx.y * hq;
+  const int tg = tid >> 5, eg = tid & 31;
+  float acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int h0 = 0; h0 < H; h0 += 32) {
-    {  // x tile: 32 tokens x 32 columns, 4 bf16 per thread
-      const int r = tid >> 3, c = (tid & 7) * 4;
-      float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-      if (t0 + r < M) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + r) * H + h0 + c);
-        v0 = bits_to_f32(xv.x << 16); v1 = bits_to_f32(xv.x & 0xFFFF0000u);
-        v2 = bits_to_f32(xv.y << 16); v3 = bits_to_f32(xv.y & 0xFFFF0000u);
-      }
-      xs[r][c] = v0; xs[r][c + 1] = v1; xs[r][c + 2] = v2; xs[r][c + 3] = v3;
-    }
+  for (int h0 = hbeg; h0 < hbeg + hq; h0 += 32) {
+    {  // x tile: 64 tokens x 32 columns; thread loads 8 columns of one token
+      const int r = tid >> 2, c = (tid & 3) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t0 + r < M) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * H + h0 + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // gate tile: 128 experts x 32 columns, 16 floats per thread
-      const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 4;
-      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + r < E) w = *reinterpret_cast<const float4*>(gate_w + (size_t)(e0 + r) * H + h0 + c);
-      ws[r][c] = w.x; ws[r][c + 1] = w.y; ws[r][c + 2] = w.z; ws[r][c + 3] = w.w;
+      for (int j = 0; j < 4; ++j) {
+        xs[c + 2 * j][r] = bits_to_f32(v[j] << 16);
+        xs[c + 2 * j + 1][r] = bits_to_f32(v[j] & 0xFFFF0000u);
+      }
+    }
+    {  // gate tile: 128 experts x 32 columns; thread loads 16 columns of one expert
+      const int r = tid >> 1, c = (tid & 1) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e0 + r < E) w = *reinterpret_cast<const float4*>(gate_w + (size_t)(e0 + r) * H + h0 + c + 4 * q);
+        ws[c + 4 * q][r] = w.x;
+        ws[c + 4 * q + 1][r] = w.y;
+        ws[c + 4 * q + 2][r] = w.z;
+        ws[c + 4 * q + 3][r] = w.w;
+      }
     }
     __syncthreads();
-    float part[4][4];
+    float p[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[i][j] = 0.0f;
+      for (int j = 0; j < 4; ++j) p[i][j] = 0.0f;
 #pragma unroll 8
     for (int kk = 0; kk < 32; ++kk) {
-      float xv[4], wv[4];
+      const float4 xa = *reinterpret_cast<const float4*>(&xs[kk][8 * tg]);
+      const float4 xb = *reinterpret_cast<const float4*>(&xs[kk][8 * tg + 4]);
+      const float4 wv = *reinterpret_cast<const float4*>(&ws[kk][4 * eg]);
+      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = xs[tt * 4 + i][kk];
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wv[j] = ws[te + 32 * j][kk];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part[i][j] = __builtin_fmaf(xv[i], wv[j], part[i][j]);
+        for (int j = 0; j < 4; ++j) p[i][j] = __builtin_fmaf(xv[i], wr[j], p[i][j]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += part[i][j];
+      for (int j = 0; j < 4; ++j) acc[i][j] += p[i][j];
     __syncthreads();
   }
+  const size_t plane = (size_t)M * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + tt * 4 + i;
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + 8 * tg + i;
     if (t >= M) continue;
+    const int e = e0 + 4 * eg;
+    float* dst = part + (size_t)blockIdx.y * plane + (size_t)t * E + e;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + te + 32 * j;
-      if (e < E) logits[(size_t)t * E + e] = acc[i][j];
-    }
+    for (int j = 0; j < 4; ++j)
+      if (e + j < E) dst[j] = acc[i][j];
   }
 }
 
@@ -240,14 +254,15 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
   }
 }
 
-int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : 1; }
+int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : kLargeParts; }
 
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
                           hipStream_t s) {
   if (M <= kSmallM) {
     router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
   } else {
-    router_logits_tiled<<<dim3((M + 31) / 32, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
+    router_logits_tiled<<<dim3((M + 63) / 64, kLargeParts, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_w,
+                                                                                            logits);
   }
 }
 
