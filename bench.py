@@ -31,6 +31,28 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (E4M3 x E2M1 i
 WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m8192": 3,
              "prefill_shared_skew_m2048": 4}
 
+# L2<->memory bytes of the w1/w3 GEMM per launch, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs (KiB per
+# dispatch). A 1 GiB device copy reads FETCH_SIZE = 524300 KiB and WRITE_SIZE = 1048576 KiB on this GPU, so the
+# fetch counter is scaled by 2.0 and the write counter by 1.0. The figures hold only for the kernel source they
+# were measured on (sha256 prefix); after any change to it the traffic is reported as null until re-measured.
+FETCH_SCALE, WRITE_SCALE = 1048576 / 524300.9, 1.0
+MEASURED_TRAFFIC = {
+    "decode_m8": dict(src="expert_gemm.hip", sha="b59c5bbc4dfd3438", fetch_kib=231548.7, write_kib=139.4),
+    "prefill_m8192": dict(src="expert_mfma.hip", sha="a3392b1143fafc40", fetch_kib=1212166.3, write_kib=118385.4),
+}
+
+
+def _measured_traffic(workload: str):
+    import hashlib
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None:
+        return None
+    path = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc", m["src"])
+    with open(path, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != m["sha"]:
+            return None
+    return int(round((m["fetch_kib"] * FETCH_SCALE + m["write_kib"] * WRITE_SCALE) * 1024))
+
 
 def _bytes_per_expert(cfg):
     """Packed MXFP4 bytes (codes + E8M0 scales) of one expert: (w1 + w3, w2)."""
@@ -169,19 +191,37 @@ def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
     if cfg.M <= 64:
         ach = gemm1_bytes / g1 / 1e9
         res["roofline"] = dict(kernel="expert_gemm1 (w1/w3 + SwiGLU + QDQ)", bound="hbm", achieved=round(ach, 1),
-                               peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                               traffic=_measured_traffic(cfg.name),
                                algorithmic_bytes=gemm1_bytes, avg_us=round(kern_us["gemm1"], 2))
     else:
         ach = gemm1_flops / g1 / 1e12
         res["roofline"] = dict(kernel="expert_gemm1 (w1/w3 + SwiGLU + QDQ)", bound="mfma", achieved=round(ach, 1),
                                peak=MFMA_FP8_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
-                               traffic=None, algorithmic_flops=gemm1_flops, avg_us=round(kern_us["gemm1"], 2))
+                               traffic=_measured_traffic(cfg.name), algorithmic_flops=gemm1_flops,
+                               avg_us=round(kern_us["gemm1"], 2))
     del L
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(budget_tokens: int = 1) -> dict:
+def calibrate_copy(gib: int = 1, reps: int = 5) -> dict:
+    """A plain device-to-device copy of a known size (the reference for the L2 byte counters)."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return dict(bytes_read=n, bytes_written=n, us=round(dt * 1e6, 1), gbs=round(2 * n / dt / 1e9, 1))
+
+
+def cpu_baseline(budget_tokens: int = 8) -> dict:
     """The CPU oracle, as it stands, on the first token(s) of the decode workload."""
     import synth
     from oracle import moe as O
@@ -210,6 +250,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the rocprof byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the layer is measured on a single MI355X (asked for --gpus {args.gpus}); "
@@ -222,6 +264,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        print(json.dumps({"calibrate_copy": calibrate_copy()}), flush=True)
+        return
     main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas)
     print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step, kernels {main_res['kernel_us']}",
           file=sys.stderr, flush=True)
