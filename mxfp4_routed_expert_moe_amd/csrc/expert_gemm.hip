@@ -262,7 +262,7 @@ struct StreamA<W_FP8_BLOCK32> {
 
 // Dynamic LDS: [64 rows][K/32] scale bytes, then the [4 waves][4 frags][4][64] fp32 partials.
 template <int WF, bool GEMM1>
-__global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
+__global__ __launch_bounds__(256, 3) void expert_gemm_stream(GemmProblem p) {   // 3 waves per SIMD (<= 170 VGPRs): measured best
   extern __shared__ __align__(16) uint8_t dyn[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
