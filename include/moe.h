@@ -22,7 +22,7 @@
  * - A workspace must not be used by two calls in flight at the same time.
  * - M = 0 is a valid empty call (returns MOE_OK, enqueues nothing).
  *
- * Supported domain: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of 128 and at most 16384, 0 <= M <= 2^24,
+ * Supported domain: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of 128 and at most 8192, 0 <= M <= 2^24,
  * M * k <= 2^26, H * I <= 2^31. E8M0 scale bytes must be in 1..254 (255 is NaN; 0 is outside the
  * supported range); E4M3 weight bytes must be finite (not 0x7F/0xFF).
  *

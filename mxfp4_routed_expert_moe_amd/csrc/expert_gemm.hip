@@ -216,12 +216,13 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 // Decode-width GEMMs on the block-scaled matrix cores (MXFP4 or FP8 weights, E4M3 activations).
 //
 // The weights stream from HBM once and feed v_mfma_scale_f32_16x16x128_f8f6f4 as stored: no
-// conversion instructions. A block owns four 16-row weight fragments (GEMM1: w1 and w3 rows of the same
-// 32 output columns, so the SwiGLU pairs and the 32-column QDQ block meet in one lane; GEMM2: 64 rows of
-// w2) and the expert's activation rows as the MFMA's 16 columns. Its four waves split the inner
-// dimension into quarters and stream 16 rows x 64 bytes per load instruction, two K steps in flight; the
-// E8M0 scales of the block's 64 rows are staged once into LDS with coalesced loads (per-step scale
-// gathers would double the L1 line traffic). The four fp32 partials are added in a fixed order in LDS.
+// conversion instructions. A block owns one expert and four 16-row weight fragments (GEMM1: w1 and w3
+// rows of the same 32 output columns, so the SwiGLU pairs and the 32-column QDQ block meet in one
+// block; GEMM2: 64 rows of w2). Wave f streams fragment f over the whole inner dimension (16 rows, each
+// a contiguous run of bytes), prefetching kStreamU steps ahead, so the only vector-memory traffic in
+// the loop is the wave's own weight rows. The E8M0 scales of the 64 rows and up to 4 activation rows
+// of the expert (E4M3 codes and scales) are staged in LDS at the start; experts with more rows are
+// processed 4 rows at a time. The four fragments meet in LDS for the epilogue.
 //
 // Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E2M1 operand
 // holds K [32g, 32g + 32) of the 128-wide step (one stored 16-byte MX block); an E4M3 operand holds
@@ -230,7 +231,8 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 // =================================================================================================
 namespace {
 
-constexpr int kStreamU = 2;   // K steps of loads in flight per lane
+constexpr int kStreamU = 4;   // K steps of weight loads in flight per lane
+constexpr int kStreamRows = 4;   // activation rows staged in LDS per pass
 
 template <int WF>
 struct StreamA;   // one 16-row x 128-K weight fragment of a lane
@@ -260,9 +262,10 @@ struct StreamA<W_FP8_BLOCK32> {
 
 }  // namespace
 
-// Dynamic LDS: [64 rows][K/32] scale bytes, then the [4 waves][4 frags][4][64] fp32 partials.
+// Dynamic LDS: scales [64][K/32], activation codes [4][K], activation scales [4][K/32], then the
+// [4 waves][64 lanes] fp32x4 exchange of the fragments.
 template <int WF, bool GEMM1>
-__global__ __launch_bounds__(256, 3) void expert_gemm_stream(GemmProblem p) {   // 3 waves per SIMD (<= 170 VGPRs): measured best
+__global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -277,110 +280,93 @@ __global__ __launch_bounds__(256, 3) void expert_gemm_stream(GemmProblem p) {   
     nrows = p.offsets[e + 1] - row0;
   }
   const int K = p.K, nk = K / 128, KB = K / 32;
-  uint8_t* sc = dyn;                                                     // [64][KB]
-  float* red = reinterpret_cast<float*>(dyn + ((64 * KB + 15) & ~15));   // [4][4][4][64]
+  uint8_t* sc = dyn;                                   // [64][KB]
+  uint8_t* xb = sc + 64 * KB;                          // [4][K]
+  uint8_t* xsb = xb + kStreamRows * K;                 // [4][KB]
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn + ((64 * KB + kStreamRows * (K + KB) + 15) & ~15));   // [4][64]
   // block rows: GEMM1 output columns c0 .. c0 + 31 (LDS rows 0..31 = w1, 32..63 = w3); GEMM2 rows c0 .. c0 + 63
   const int c0 = GEMM1 ? blockIdx.x * 32 : blockIdx.x * 64;
   auto grow_of = [&](int r) { return GEMM1 ? c0 + (r & 31) : c0 + r; };
-  auto sbase_of = [&](int r) -> const uint8_t* {
-    const uint8_t* sb = (GEMM1 && r >= 32) ? p.sb : p.sa;
-    return (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
-                           : sb + (size_t)(grow_of(r) / 32) * KB;
-  };
   const size_t wrow_bytes = (WF == W_MXFP4) ? (size_t)K / 2 : (size_t)K;
-  const uint8_t* wrow[4];
-  int lrow[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    lrow[f] = GEMM1 ? 32 * (f >> 1) + 16 * (f & 1) + r16 : 16 * f + r16;
-    const uint8_t* wb = static_cast<const uint8_t*>((GEMM1 && f >= 2) ? p.wb : p.wa);
-    wrow[f] = wb + (size_t)e * p.w_expert_stride + (size_t)grow_of(lrow[f]) * wrow_bytes;
-  }
-  // stage the scales: KB/4 dwords per row (KB is a multiple of 4)
-  for (int i = threadIdx.x; i < 64 * (KB / 4); i += 256) {
-    const int r = i / (KB / 4), c = i % (KB / 4);
-    *reinterpret_cast<uint32_t*>(sc + r * KB + 4 * c) = *reinterpret_cast<const uint32_t*>(sbase_of(r) + 4 * c);
-  }
-  __syncthreads();
-  const int kb = nk * wave / 4, ke = nk * (wave + 1) / 4;
+  const int lrow = (GEMM1 ? 32 * (wave >> 1) + 16 * (wave & 1) : 16 * wave) + r16;   // this wave's fragment
+  const uint8_t* wrow = static_cast<const uint8_t*>((GEMM1 && wave >= 2) ? p.wb : p.wa) +
+                        (size_t)e * p.w_expert_stride + (size_t)grow_of(lrow) * wrow_bytes;
 
-  for (int tg = 0; tg < nrows; tg += 16) {
-    const bool valid = tg + r16 < nrows;
-    const int pos = row0 + tg + r16;
-    int arow = 0;
-    if (valid) arow = (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
-    const uint8_t* brow = p.act_q + (size_t)arow * K;
-    const uint8_t* bsrow = p.act_s + (size_t)arow * KB;
-    f32x4 acc[4];
+  for (int tg = 0; tg < nrows; tg += kStreamRows) {
+    const int n = min(kStreamRows, nrows - tg);
+    // the first weight batch goes out before the staging, so HBM is busy from the start
+    StreamA<WF> A[kStreamU];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ks0 = kb; ks0 < ke; ks0 += kStreamU) {
-      StreamA<WF> A[kStreamU][4];
-      u32x4 b0[kStreamU], b1[kStreamU];
-      uint32_t bs[kStreamU];
-#pragma unroll
-      for (int u = 0; u < kStreamU; ++u) {
-        const int ks = ks0 + u;
-        if (ks < ke) {
-#pragma unroll
-          for (int f = 0; f < 4; ++f) A[u][f].load(wrow[f], ks, g);
-          if (valid) {
-            b0[u] = *reinterpret_cast<const u32x4*>(brow + ks * 128 + 16 * g);
-            b1[u] = *reinterpret_cast<const u32x4*>(brow + ks * 128 + 64 + 16 * g);
-            bs[u] = bsrow[4 * ks + g];
-          } else {
-            b0[u] = u32x4{0u, 0u, 0u, 0u};
-            b1[u] = b0[u];
-            bs[u] = 127u;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kStreamU; ++u) {
-        const int ks = ks0 + u;
-        if (ks < ke) {
-          const i32x8 B = i32x8{(int)b0[u][0], (int)b0[u][1], (int)b0[u][2], (int)b0[u][3],
-                                (int)b1[u][0], (int)b1[u][1], (int)b1[u][2], (int)b1[u][3]};
-#pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[u][f].frag(), B, acc[f], StreamA<WF>::kFmt, 0,
-                                                                      0, (int)sc[lrow[f] * KB + 4 * ks + g], 0,
-                                                                      (int)bs[u]);
-        }
+    for (int u = 0; u < kStreamU; ++u)
+      if (u < nk) A[u].load(wrow, u, g);
+    if (tg == 0) {   // scales of the block's 64 weight rows: KB/4 dwords per row (KB is a multiple of 4)
+      for (int i = threadIdx.x; i < 64 * (KB / 4); i += 256) {
+        const int r = i / (KB / 4), c = i % (KB / 4);
+        const uint8_t* sb = (GEMM1 && r >= 32) ? p.sb : p.sa;
+        const uint8_t* src = (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
+                                             : sb + (size_t)(grow_of(r) / 32) * KB;
+        *reinterpret_cast<uint32_t*>(sc + r * KB + 4 * c) = *reinterpret_cast<const uint32_t*>(src + 4 * c);
       }
     }
-    // fixed-order sum of the four K quarters
+    auto act_row = [&](int t) {   // activation row of staged row t (rows past n repeat the first)
+      const int pos = row0 + tg + (t < n ? t : 0);
+      return (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
+    };
+    for (int i = threadIdx.x; i < kStreamRows * (K / 16); i += 256) {
+      const int t = i / (K / 16), c = i % (K / 16);
+      *reinterpret_cast<u32x4*>(xb + t * K + 16 * c) =
+          *reinterpret_cast<const u32x4*>(p.act_q + (size_t)act_row(t) * K + 16 * c);
+    }
+    for (int i = threadIdx.x; i < kStreamRows * (KB / 4); i += 256) {
+      const int t = i / (KB / 4), c = i % (KB / 4);
+      *reinterpret_cast<uint32_t*>(xsb + t * KB + 4 * c) =
+          *reinterpret_cast<const uint32_t*>(p.act_s + (size_t)act_row(t) * KB + 4 * c);
+    }
+    __syncthreads();
+    const int bt = r16 & (kStreamRows - 1);   // lanes past the staged rows compute a staged row (discarded)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks0 = 0; ks0 < nk; ks0 += kStreamU) {
+      StreamA<WF> An[kStreamU];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+      for (int u = 0; u < kStreamU; ++u)
+        if (ks0 + kStreamU + u < nk) An[u].load(wrow, ks0 + kStreamU + u, g);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[((wave * 4 + f) * 4 + v) * 64 + lane] = acc[f][v];
+      for (int u = 0; u < kStreamU; ++u) {
+        const int ks = ks0 + u;
+        if (ks < nk) {
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(xb + bt * K + ks * 128 + 16 * g);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + bt * K + ks * 128 + 64 + 16 * g);
+          const i32x8 B = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2],
+                                (int)b1[3]};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[u].frag(), B, acc, StreamA<WF>::kFmt, 0, 0,
+                                                                 (int)sc[lrow * KB + 4 * ks + g], 0,
+                                                                 (int)xsb[bt * KB + 4 * ks + g]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) A[u] = An[u];
+    }
+    // the four fragments meet in LDS; wave 0 runs the epilogue (lane: weight rows 4g..4g+3, row r16)
+    xch[wave * 64 + lane] = acc;
     __syncthreads();
     if (wave == 0) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float s = red[((0 * 4 + f) * 4 + v) * 64 + lane];
-          s = s + red[((1 * 4 + f) * 4 + v) * 64 + lane];
-          s = s + red[((2 * 4 + f) * 4 + v) * 64 + lane];
-          s = s + red[((3 * 4 + f) * 4 + v) * 64 + lane];
-          acc[f][v] = s;
-        }
-      // lane holds weight rows 4g + v of each fragment for activation row r16
+      const f32x4 a0 = xch[lane], a1 = xch[64 + lane], a2 = xch[128 + lane], a3 = xch[192 + lane];
+      const bool valid = r16 < n;
+      const int pos = row0 + tg + r16;
       if constexpr (GEMM1) {
         float rwv = 1.0f;
         if (valid && !p.dense) rwv = p.rw[p.pairs[pos]];
+        const f32x4 gf[2] = {a0, a1}, uf[2] = {a2, a3};
         float h[2][4];
         float amax = 0.0f;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float gv = round_bf16(acc[half][v]);
-            const float uv = round_bf16(acc[2 + half][v]);
-            h[half][v] = round_bf16(swiglu(gv, uv, rwv, !p.dense));
+            h[half][v] = round_bf16(swiglu(round_bf16(gf[half][v]), round_bf16(uf[half][v]), rwv, !p.dense));
             amax = fmaxf(amax, fabsf(h[half][v]));
           }
+        // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const int E8 = qdq_exponent(amax);
@@ -399,20 +385,24 @@ __global__ __launch_bounds__(256, 3) void expert_gemm_stream(GemmProblem p) {   
         if (valid) {
           const int orow = p.dense ? pos : p.pairs[pos];
           uint16_t* o = p.out + (size_t)orow * p.N + c0 + 4 * g;
+          const f32x4 af[4] = {a0, a1, a2, a3};
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[f][0])) | (uint32_t(f32_to_bf16_rne(acc[f][1])) << 16);
-            const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[f][2])) | (uint32_t(f32_to_bf16_rne(acc[f][3])) << 16);
+            const uint32_t lo = uint32_t(f32_to_bf16_rne(af[f][0])) | (uint32_t(f32_to_bf16_rne(af[f][1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16_rne(af[f][2])) | (uint32_t(f32_to_bf16_rne(af[f][3])) << 16);
             *reinterpret_cast<u32x2*>(o + 16 * f) = u32x2{lo, hi};
           }
         }
       }
     }
-    __syncthreads();   // the partials buffer is reused by the next row group
+    __syncthreads();   // staging and exchange buffers are reused by the next row group
   }
 }
 
-size_t stream_lds_bytes(int K) { return (size_t)((64 * (K / 32) + 15) & ~15) + 4 * 4 * 4 * 64 * sizeof(float); }
+size_t stream_lds_bytes(int K) {
+  const int KB = K / 32;
+  return (size_t)((64 * KB + kStreamRows * (K + KB) + 15) & ~15) + 4 * 64 * sizeof(f32x4);
+}
 
 template <bool GEMM1>
 static void launch_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s) {

@@ -70,7 +70,7 @@ moe_status check_dims(const moe_dims* d, int32_t M) {
   if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || !std::isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
   if (E > 256 || k > 8 || k > E) return MOE_ERR_UNSUPPORTED;
   if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (H > 16384 || I > 16384) return MOE_ERR_UNSUPPORTED;   // per-block scale staging fits in LDS
+  if (H > 8192 || I > 8192) return MOE_ERR_UNSUPPORTED;   // decode-width LDS staging stays within 64 KB
   if ((int64_t)H * I > (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (M > (1 << 24) || (int64_t)M * k > (int64_t(1) << 26)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;

@@ -420,3 +420,20 @@ def test_prefill_path_runs_are_bit_identical():
     a = forward(cfg, d)["out_bits"]
     for _ in range(2):
         assert np.array_equal(forward(cfg, d)["out_bits"], a)
+
+
+@pytest.mark.parametrize("M", [1, 5, 37, 64])
+def test_decode_width_with_fp8_shared_expert(M):
+    """Decode-width routed experts plus the FP8 shared expert (both through the weight-streaming kernel),
+    every token against the oracle; the routed-only and shared-only parts checked on their own too."""
+    cfg, inp, d = cfg_inputs(0, M=M, H=512, I=256, E=8, k=2, shared=True)
+    assert cfg.M * cfg.k < 32 * cfg.E
+    res = forward(cfg, d)
+    ref = O.moe_forward(inp, cfg)
+    diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
+    if diff.size:
+        ref = O.moe_forward(inp, cfg, ids=res["ids"], rw=res["rw"])
+    assert_within(res["out"], ref["out"], f"M={M} layer with shared expert")
+    assert_within(res["shared_out"], ref["shared_y"], f"M={M} shared expert")
+    routed = forward(cfg, d, with_shared=False)
+    assert_within(routed["out"], O.combine(ref["ids"], ref["slot_y"], None), f"M={M} routed part")
