@@ -437,3 +437,34 @@ def test_decode_width_with_fp8_shared_expert(M):
     assert_within(res["shared_out"], ref["shared_y"], f"M={M} shared expert")
     routed = forward(cfg, d, with_shared=False)
     assert_within(routed["out"], O.combine(ref["ids"], ref["slot_y"], None), f"M={M} routed part")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 10, 15, 20, 32])
+def test_verifier_widths_full_size_layer(M):
+    """The full-size layer (hidden 5120, 128 MXFP4 experts, intermediate 2304, top-6) at the speculative
+    verifier widths: routing bit-exact except documented ties, outputs within tolerance on sampled tokens."""
+    cfg, inp, d = cfg_inputs(2)
+    c = synth.get_config(2, M=M)
+    res = forward(c, d, M=M)
+    sub = dict(inp)
+    sub["x"] = inp["x"][:M]
+    full = O.route(sub["x"], inp["gate_w"], inp["gate_b"], c.k, c.route_scale)
+    diff = check_routing(res["ids"], res["rw"], full, c)
+    toks = np.unique(np.array([0, M - 1, M // 2]))
+    ref = O.moe_forward(sub, c, tokens=toks, ids=res["ids"][toks] if diff.size else None,
+                        rw=res["rw"][toks] if diff.size else None)
+    assert_within(res["out"][toks], ref["out"], f"M={M}")
+
+
+def test_decode_path_is_batch_invariant():
+    """Within the decode-width path a token's routing and output do not depend on the other tokens of
+    the batch: the first 8 tokens give the same bits alone, in a batch of 32, and in a batch of 64."""
+    cfg, inp, d = cfg_inputs(2)
+    outs = {}
+    for M in (8, 32, 64):
+        c = synth.get_config(2, M=M)
+        r = forward(c, d, M=M)
+        outs[M] = (r["ids"][:8], r["out_bits"][:8])
+    for M in (32, 64):
+        assert np.array_equal(outs[M][0], outs[8][0]), f"routing of the first tokens changes with M={M}"
+        assert np.array_equal(outs[M][1], outs[8][1]), f"outputs of the first tokens change with M={M}"
