@@ -234,6 +234,21 @@ namespace {
 constexpr int kStreamU = 4;   // K steps of weight loads in flight per lane
 constexpr int kStreamRows = 4;   // activation rows staged in LDS per pass
 
+// Direct global -> LDS copy of a run of nbytes (a multiple of UNIT = 16 or 4) by one wave: lane i moves
+// UNIT bytes of every 64 * UNIT-byte piece (the copy lands at lds + off + i * UNIT). Every copy of the
+// run is issued before any is waited for.
+template <int UNIT>
+__device__ __forceinline__ void stage_run(uint8_t* lds, const uint8_t* src, int nbytes, int lane) {
+  static_assert(UNIT == 16 || UNIT == 4, "direct-to-LDS copies move 16 or 4 bytes per lane");
+  for (int off = 0; off < nbytes; off += 64 * UNIT)
+    if (off + UNIT * lane < nbytes) {
+      const void* g = static_cast<const void*>(src + off + UNIT * lane);
+      auto* l = (__attribute__((address_space(3))) void*)(lds + off);
+      if constexpr (UNIT == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+    }
+}
+
 template <int WF>
 struct StreamA;   // one 16-row x 128-K weight fragment of a lane
 template <>
@@ -294,35 +309,41 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
 
   for (int tg = 0; tg < nrows; tg += kStreamRows) {
     const int n = min(kStreamRows, nrows - tg);
-    // the first weight batch goes out before the staging, so HBM is busy from the start
-    StreamA<WF> A[kStreamU];
-#pragma unroll
-    for (int u = 0; u < kStreamU; ++u)
-      if (u < nk) A[u].load(wrow, u, g);
-    if (tg == 0) {   // scales of the block's 64 weight rows: KB/4 dwords per row (KB is a multiple of 4)
-      for (int i = threadIdx.x; i < 64 * (KB / 4); i += 256) {
-        const int r = i / (KB / 4), c = i % (KB / 4);
-        const uint8_t* sb = (GEMM1 && r >= 32) ? p.sb : p.sa;
-        const uint8_t* src = (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
-                                             : sb + (size_t)(grow_of(r) / 32) * KB;
-        *reinterpret_cast<uint32_t*>(sc + r * KB + 4 * c) = *reinterpret_cast<const uint32_t*>(src + 4 * c);
+    // staging: runs of contiguous bytes copied straight into LDS, one run per wave in turn, all in
+    // flight together. Run 0/1: the weight scales (MXFP4: the 64 rows' E8M0 bytes, two K-byte runs for
+    // GEMM1 (w1, w3 rows) or one 2K-byte run for GEMM2; FP8: the two 32-row blocks' scale rows). Then
+    // the n activation rows and their scales. Staged rows past n are not written: the lanes that read
+    // them produce output columns that the epilogue discards.
+    {
+      int run = 0;
+      auto mine = [&]() { return (run++ & 3) == wave; };
+      if (tg == 0) {
+        if constexpr (WF == W_MXFP4) {
+          const uint8_t* s1 = p.sa + (size_t)e * p.s_expert_stride + (size_t)c0 * KB;
+          if (GEMM1) {
+            if (mine()) stage_run<16>(sc, s1, 32 * KB, lane);
+            if (mine()) stage_run<16>(sc + 32 * KB, p.sb + (size_t)e * p.s_expert_stride + (size_t)c0 * KB, 32 * KB, lane);
+          } else {
+            if (mine()) stage_run<16>(sc, s1, 64 * KB, lane);
+          }
+        } else {   // 32 x 32 blocks: one scale row per 32 weight rows
+          if (mine()) stage_run<4>(sc, p.sa + (size_t)(c0 / 32) * KB, KB, lane);
+          if (mine()) stage_run<4>(sc + KB, (GEMM1 ? p.sb + (size_t)(c0 / 32) * KB : p.sa + (size_t)(c0 / 32 + 1) * KB), KB, lane);
+        }
+      }
+      for (int t = 0; t < n; ++t) {
+        const int pos = row0 + tg + t;
+        const int arow = (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
+        if (mine()) stage_run<16>(xb + t * K, p.act_q + (size_t)arow * K, K, lane);
+        if (mine()) stage_run<4>(xsb + t * KB, p.act_s + (size_t)arow * KB, KB, lane);
       }
     }
-    auto act_row = [&](int t) {   // activation row of staged row t (rows past n repeat the first)
-      const int pos = row0 + tg + (t < n ? t : 0);
-      return (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
-    };
-    for (int i = threadIdx.x; i < kStreamRows * (K / 16); i += 256) {
-      const int t = i / (K / 16), c = i % (K / 16);
-      *reinterpret_cast<u32x4*>(xb + t * K + 16 * c) =
-          *reinterpret_cast<const u32x4*>(p.act_q + (size_t)act_row(t) * K + 16 * c);
-    }
-    for (int i = threadIdx.x; i < kStreamRows * (KB / 4); i += 256) {
-      const int t = i / (KB / 4), c = i % (KB / 4);
-      *reinterpret_cast<uint32_t*>(xsb + t * KB + 4 * c) =
-          *reinterpret_cast<const uint32_t*>(p.act_s + (size_t)act_row(t) * KB + 4 * c);
-    }
-    __syncthreads();
+    // the first weight batch (in bounds for any nk: short K repeats the last step)
+    StreamA<WF> A[kStreamU];
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) A[u].load(wrow, min(u, nk - 1), g);
+    // every copy of this wave has landed in LDS (vmcnt counts the LDS-bound loads too); then meet
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int bt = r16 & (kStreamRows - 1);   // lanes past the staged rows compute a staged row (discarded)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int ks0 = 0; ks0 < nk; ks0 += kStreamU) {
@@ -339,7 +360,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
           const i32x8 B = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2],
                                 (int)b1[3]};
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[u].frag(), B, acc, StreamA<WF>::kFmt, 0, 0,
-                                                                 (int)sc[lrow * KB + 4 * ks + g], 0,
+                                                                 (int)sc[(WF == W_MXFP4 ? lrow : lrow >> 5) * KB + 4 * ks + g], 0,
                                                                  (int)xsb[bt * KB + 4 * ks + g]);
         }
       }

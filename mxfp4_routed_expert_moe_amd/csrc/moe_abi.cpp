@@ -91,7 +91,7 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
   } while (0)
 
 moe_status check_packed(const moe_mxfp4_experts* w) {
-  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !w->s1 || !w->s3 || !w->s2)
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -102,7 +102,7 @@ moe_status check_decoded(const moe_bf16_experts* w) {
 }
 
 moe_status check_shared(const moe_fp8_expert* w) {
-  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !w->s1 || !w->s3 || !w->s2)
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16))
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
@@ -255,7 +255,7 @@ moe_status moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const f
                      int32_t* ids, float* rw, uint8_t* x_q, uint8_t* x_s, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(dims, M));
   if (M == 0) return MOE_OK;
-  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(ids, 4) || !al(rw, 4) || !al(x_q, 16) || !x_s)
+  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(ids, 4) || !al(rw, 4) || !al(x_q, 16) || !al(x_s, 16))
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   do_route(dims, M, x, gate_w, gate_b, ids, rw, x_q, x_s, ws, static_cast<hipStream_t>(stream));
@@ -281,7 +281,7 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
   if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
-  if (!al(x_q, 16) || !x_s || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
+  if (!al(x_q, 16) || !al(x_s, 16) || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
     return MOE_ERR_INVALID_ARG;
   if ((h_q == nullptr) != (h_s == nullptr)) return MOE_ERR_INVALID_ARG;
   if (h_q != nullptr && !al(h_q, 16)) return MOE_ERR_INVALID_ARG;
@@ -304,8 +304,8 @@ moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q,
   if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
-  if (!al(x_q, 16) || !x_s || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(h_q, 16) ||
-      !h_s)
+  if (!al(x_q, 16) || !al(x_s, 16) || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(h_q, 16) ||
+      !al(h_s, 16))
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -323,7 +323,7 @@ moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q,
   if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
-  if (!al(h_q, 16) || !h_s || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
+  if (!al(h_q, 16) || !al(h_s, 16) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) || !al(slot_out, 16))
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -339,7 +339,7 @@ moe_status moe_shared_expert(const moe_dims* dims, int32_t M, const uint8_t* x_q
   MOE_TRY(check_dims(dims, M));
   if (M == 0) return MOE_OK;
   MOE_TRY(check_shared(shared));
-  if (!al(x_q, 16) || !x_s || !al(shared_out, 16)) return MOE_ERR_INVALID_ARG;
+  if (!al(x_q, 16) || !al(x_s, 16) || !al(shared_out, 16)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   const WsLayout L = ws_layout(dims, M);
   do_shared(dims, M, x_q, x_s, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), shared_out,
@@ -400,7 +400,7 @@ moe_status moe_expand_mxfp4(int64_t rows, int32_t cols, const uint8_t* w, const 
   if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
   if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
-  if (!al(w, 16) || !s || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (!al(w, 16) || !al(s, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
   moe::launch_expand_mxfp4(rows, cols, w, s, out, static_cast<hipStream_t>(stream));
   return launched();
 }

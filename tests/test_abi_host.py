@@ -93,7 +93,10 @@ def _forward(lib, dims, M, x=FAKE, gw=FAKE, gb=FAKE, packed=True, decoded=False,
              ws_bytes=1 << 40, shared_out=None):
     f = lib.moe_forward
     f.restype = ctypes.c_int32
-    pk = ctypes.byref(Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)) if packed else None
+    if isinstance(packed, Six):
+        pk = ctypes.byref(packed)
+    else:
+        pk = ctypes.byref(Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)) if packed else None
     dc = ctypes.byref(Three(FAKE, FAKE, FAKE)) if decoded else None
     sh = ctypes.byref(shared) if shared is not None else None
     return f(ctypes.byref(dims), ctypes.c_int32(M), ctypes.c_void_p(x), ctypes.c_void_p(gw), ctypes.c_void_p(gb), pk,
@@ -114,6 +117,8 @@ def test_forward_refuses_before_launch(lib):
     assert _forward(lib, d, 8, ws_bytes=1024) == WORKSPACE               # workspace too small
     assert _forward(lib, d, 8, shared=Six(FAKE, FAKE, FAKE, 0, FAKE, FAKE)) == INVALID   # partial shared set
     assert _forward(lib, d, 8, shared_out=FAKE) == INVALID               # shared_out without a shared expert
+    assert _forward(lib, d, 8, packed=Six(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE)) == INVALID   # misaligned scales
+    assert _forward(lib, d, 8, shared=Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8)) == INVALID  # misaligned scales
     assert _forward(lib, Dims(128, 5120, 2304, 9, 1.5), 8) == UNSUPPORTED
     assert _forward(lib, Dims(512, 5120, 2304, 6, 1.5), 8) == UNSUPPORTED
     assert _forward(lib, Dims(128, 5056, 2304, 6, 1.5), 8) == UNSUPPORTED
