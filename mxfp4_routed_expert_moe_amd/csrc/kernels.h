@@ -10,12 +10,17 @@
 namespace moe {
 
 // ---- router (route.hip) --------------------------------------------------------------------
+// Batches of at most kRouterSmallM tokens take the decode-width router: the logits kernel also does
+// the per-32 E4M3 QDQ of x, and the selection may run fused with the permutation.
+constexpr int kRouterSmallM = 64;
 // fp32 logits of the raw bf16 activations against the fp32 gate weight [E, H], as
 // router_logit_parts(M, H) partial planes [parts, M, E] (summed in order by the select kernel).
+// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise).
 int router_logit_parts(int M, int H);
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          hipStream_t s);
-// sqrt(softplus) scores, biased top-k, normalised route weights; plus the per-32 E4M3 QDQ of x.
+                          uint8_t* x_q, uint8_t* x_s, hipStream_t s);
+// sqrt(softplus) scores, biased top-k, normalised route weights; at M > kRouterSmallM also the
+// per-32 E4M3 QDQ of x.
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
                               uint8_t* x_q, uint8_t* x_s, hipStream_t s);
@@ -24,6 +29,11 @@ void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, con
 // Stable counting sort of the M*k (token, slot) pairs by expert id.
 void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                     int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
+// M <= kRouterSmallM only: the router's selection (from the partial logit planes) and the counting sort in
+// one block; ids and rw equal launch_router_select_qdq's bit for bit.
+void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
+                                 const float* gate_b, int32_t* ids, float* rw, int32_t* counts,
+                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
 
 // ---- expert GEMMs (expert_gemm.hip) --------------------------------------------------------
 enum WeightFormat { W_MXFP4 = 0, W_FP8_BLOCK32 = 1, W_BF16 = 2 };

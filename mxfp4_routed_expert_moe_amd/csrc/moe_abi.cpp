@@ -140,7 +140,7 @@ void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, cons
               float* rw, uint8_t* xq, uint8_t* xs, void* ws, hipStream_t s) {
   const WsLayout L = ws_layout(d, M);
   float* logits = at<float>(ws, L.logits);
-  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, s);
+  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, xq, xs, s);
   moe::launch_router_select_qdq(M, d->hidden, d->num_experts, d->top_k, d->route_scale, logits, gb, x, ids, rw, xq,
                                 xs, s);
 }
@@ -377,12 +377,20 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
   float* rw = rw_out ? rw_out : at<float>(ws, L.rw);
   uint8_t* xq = at<uint8_t>(ws, L.x_q);
   uint8_t* xs = at<uint8_t>(ws, L.x_s);
-  do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* pairs = at<int32_t>(ws, L.pairs);
   int32_t* active = at<int32_t>(ws, L.active);
-  moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
-                      at<int32_t>(ws, L.inv), active, s);
+  if (M <= moe::kRouterSmallM) {   // decode widths: logits + QDQ, then selection and permutation in one block
+    float* logits = at<float>(ws, L.logits);
+    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, s);
+    moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
+                                     gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
+                                     at<int32_t>(ws, L.inv), active, s);
+  } else {
+    do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
+    moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
+                        at<int32_t>(ws, L.inv), active, s);
+  }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, at<uint8_t>(ws, L.h_q),
                 at<uint8_t>(ws, L.h_s), ws, s);

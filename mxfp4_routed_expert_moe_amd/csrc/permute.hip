@@ -7,6 +7,7 @@
 // pairs of expert e with wave ballots.
 #include "kernels.h"
 #include "moe_device.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -75,19 +76,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
 // same id (one LDS sweep per thread).
 constexpr int kSmallPairs = 1024;
 
-__global__ __launch_bounds__(1024) void permute_small_kernel(int P, int E, const int32_t* __restrict__ ids,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
-                                                             int32_t* __restrict__ active) {
-  __shared__ int sid[kSmallPairs];
-  __shared__ int hist[256];
-  __shared__ int scan[256];
-  __shared__ int ascan[256];
+// Thread tid holds the id of pair tid in v (-1 past P); sid, hist, scan, ascan are the block's LDS.
+// Called by all threads of the block.
+__device__ __forceinline__ void counting_sort_small(int P, int E, int v, int* sid, int* hist, int* scan, int* ascan,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
+                                                    int32_t* __restrict__ active) {
   const int tid = threadIdx.x;
   if (tid < 256) hist[tid] = 0;
-  int v = -1;
-  if (tid < P) v = ids[tid];
   const bool ok = v >= 0 && v < E;
   sid[tid] = ok ? v : -1;
   __syncthreads();
@@ -129,12 +125,96 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(int P, int E, const
   }
 }
 
+__global__ __launch_bounds__(1024) void permute_small_kernel(int P, int E, const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
+                                                             int32_t* __restrict__ active) {
+  __shared__ int sid[kSmallPairs];
+  __shared__ int hist[256];
+  __shared__ int scan[256];
+  __shared__ int ascan[256];
+  const int v = threadIdx.x < P ? ids[threadIdx.x] : -1;
+  counting_sort_small(P, E, v, sid, hist, scan, ascan, counts, offsets, pairs, inv, active);
+}
+
+// Decode widths (M <= 64): wave w selects the experts of tokens w, w + 16, ... with the router's own
+// selection code (so ids and route weights equal the separate select kernel's bit for bit). A token's
+// k experts are distinct, so expert e's pairs are one per token: bit t of the LDS mask of expert e says
+// that token t chose it. The count is the mask's popcount, and the stable rank of pair (t, j) inside its
+// expert is the number of set bits below t. One wave scans the counts; no per-pair sweep.
+__global__ __launch_bounds__(1024) void select_permute_small_kernel(
+    int M, int E, int k, float route_scale, int nparts, const float* __restrict__ logits,
+    const float* __restrict__ gate_b, int32_t* __restrict__ ids, float* __restrict__ rw, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
+    int32_t* __restrict__ active) {
+  __shared__ int sid[kSmallPairs];
+  __shared__ unsigned long long emask[256];
+  __shared__ int soff[256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < 256) emask[tid] = 0ull;
+  __syncthreads();
+  for (int t = wave; t < M; t += kSmallPairs / 64)
+    select_token(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, sid, emask);
+  __syncthreads();
+  if (wave == 0) {   // counts, offsets and the active list: lane l owns experts 4l .. 4l + 3
+    int c[4], csum = 0, fsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? __popcll(emask[e]) : 0;
+      csum += c[i];
+      fsum += c[i] > 0 ? 1 : 0;
+    }
+    int ic = csum, ifl = fsum;   // inclusive scans over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(ic, off, 64), b = __shfl_up(ifl, off, 64);
+      if (lane >= off) {
+        ic += a;
+        ifl += b;
+      }
+    }
+    int oc = ic - csum, of = ifl - fsum;
+    const int total = __shfl(ic, 63, 64), n_active = __shfl(ifl, 63, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) {
+        counts[e] = c[i];
+        offsets[e] = oc;
+        soff[e] = oc;
+        if (c[i] > 0) active[of++] = e;   // positions < n_active
+        oc += c[i];
+      }
+    }
+    for (int i = n_active + lane; i < E; i += 64) active[i] = -1;   // padding, disjoint from the above
+    if (lane == 0) offsets[E] = total;
+  }
+  __syncthreads();
+  const int P = M * k;
+  if (tid < P) {
+    const int t = tid / k, v = sid[tid];
+    const int pos = soff[v] + __popcll(emask[v] & ((1ull << t) - 1ull));
+    pairs[pos] = tid;
+    if (inv) inv[tid] = pos;
+  }
+}
+
 void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets, int32_t* pairs,
                     int32_t* inv, int32_t* active, hipStream_t s) {
   if (P <= kSmallPairs)
     permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
   else
     permute_kernel<<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+}
+
+void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
+                                 const float* gate_b, int32_t* ids, float* rw, int32_t* counts,
+                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s) {
+  select_permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, router_logit_parts(M, H),
+                                                                     logits, gate_b, ids, rw, counts, offsets, pairs,
+                                                                     inv, active);
 }
 
 }  // namespace moe

@@ -13,32 +13,45 @@
 // the k weights in slot order.
 #include "kernels.h"
 #include "moe_device.h"
+#include "route_device.h"
 
 namespace moe {
 
-constexpr int kSmallM = 64;
+constexpr int kSmallM = kRouterSmallM;
 constexpr int kChunkH = 512;   // H columns per partial logit at small M
 
 // Small M: one wave per (expert, 512-wide chunk of H); lane l covers 8 consecutive columns. Every
 // wave handles all M <= 64 tokens, so each gate element is read once. The wave's fp32 partial sum
 // (8 FMA chain per lane, then a butterfly over the 64 lanes) goes to part[chunk][t][e]; the select
-// kernel adds the chunks in ascending order.
+// kernel adds the chunks in ascending order. The same blocks also QDQ the rows of x: block (b, chunk)
+// takes the chunk's 32-wide blocks of tokens b, b + gridDim.x, ...
 __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, const uint16_t* __restrict__ x,
                                                            const float* __restrict__ gate_w,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part, uint8_t* __restrict__ x_q,
+                                                           uint8_t* __restrict__ x_s) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int chunk = blockIdx.y;
-  if (e >= E) return;
   const int h = chunk * kChunkH + lane * 8;
-  const bool ok = h < H;
+  const bool ok = h < H && e < E;
   float4 w0 = make_float4(0.f, 0.f, 0.f, 0.f), w1 = w0;
-  if (ok) {
+  if (ok) {   // the gate loads go out first
     w0 = *reinterpret_cast<const float4*>(gate_w + (size_t)e * H + h);
     w1 = *reinterpret_cast<const float4*>(gate_w + (size_t)e * H + h + 4);
   }
+  {  // the QDQ of this chunk's 32-wide blocks of tokens blockIdx.x, blockIdx.x + gridDim.x, ...
+    const int nb = min(kChunkH, H - chunk * kChunkH) / 32, b0 = chunk * (kChunkH / 32);
+    for (int it = threadIdx.x;; it += 256) {
+      const int t = blockIdx.x + (it / nb) * gridDim.x, b = b0 + it % nb;
+      if (t >= M) break;
+      qdq_block32(x + (size_t)t * H + b * 32, x_q + (size_t)t * H + b * 32, x_s + (size_t)t * (H / 32) + b);
+    }
+  }
+  if (e >= E) return;
   const size_t plane = (size_t)M * E;
-  for (int t = 0; t < M; ++t) {
+  // one token's partial: an 8-FMA chain per lane, then a butterfly over the 64 lanes. Four tokens at a
+  // time, so that their butterflies overlap (each token's order is unchanged).
+  auto dot8 = [&](int t) {
     float a = 0.0f;
     if (ok) {
       const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h);
@@ -51,6 +64,23 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
       a = __builtin_fmaf(bits_to_f32(xv[3] << 16), w1.z, a);
       a = __builtin_fmaf(bits_to_f32(xv[3] & 0xFFFF0000u), w1.w, a);
     }
+    return a;
+  };
+  int t = 0;
+  for (; t + 4 <= M; t += 4) {
+    float a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = dot8(t + u);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += __shfl_xor(a[u], off, 64);
+    if (lane == 0)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) part[(size_t)chunk * plane + (size_t)(t + u) * E + e] = a[u];
+  }
+  for (; t < M; ++t) {
+    float a = dot8(t);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
     if (lane == 0) part[(size_t)chunk * plane + (size_t)t * E + e] = a;
@@ -138,128 +168,30 @@ __global__ __launch_bounds__(256) void router_logits_tiled(int M, int H, int E, 
   }
 }
 
-struct Cand { float v; float s; int i; };
-
-__device__ __forceinline__ Cand better(Cand a, Cand b) {
-  // larger selection score wins; equal scores go to the lower expert id
-  return (a.v > b.v || (a.v == b.v && a.i < b.i)) ? a : b;
-}
-
-// One block per token. Wave 0: scores, biased top-k, normalisation; all four waves: the QDQ of the
-// token's row (one 32-wide block per thread).
+// One block per token. Wave 0: scores, biased top-k, normalisation; at M > 64 all four waves also
+// QDQ the token's row (one 32-wide block per thread); at M <= 64 the logits kernel has done it.
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
                                                          int nparts, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
                                                          const uint16_t* __restrict__ x,
                                                          int32_t* __restrict__ ids, float* __restrict__ rw,
                                                          uint8_t* __restrict__ x_q, uint8_t* __restrict__ x_s) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x;
-  if (threadIdx.x < 64) {
-  // ---- scores and selection values: lane owns experts lane, lane + 64, ... (E <= 256)
-  float sc[4], sel[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    sc[j] = 0.0f; sel[j] = -INFINITY;
-    if (e < E) {
-      // partial logits added in ascending chunk order; four loads in flight at a time
-      const float* lp = logits + (size_t)t * E + e;
-      const size_t plane = (size_t)M * E;
-      float l = lp[0];
-      int c = 1;
-      for (; c + 3 < nparts; c += 4) {
-        const float a0 = lp[c * plane], a1 = lp[(c + 1) * plane], a2 = lp[(c + 2) * plane], a3 = lp[(c + 3) * plane];
-        l = l + a0;
-        l = l + a1;
-        l = l + a2;
-        l = l + a3;
-      }
-      for (; c < nparts; ++c) l = l + lp[c * plane];
-      const float sp = l > 20.0f ? l : log1pf(expf(l));
-      sc[j] = sqrtf(sp);
-      sel[j] = sc[j] + gate_b[e];
-    }
-  }
-  float wsel[8];
-  int isel[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    wsel[r] = 0.0f;
-    isel[r] = 0;
-    if (r >= k) continue;
-    Cand c{-INFINITY, 0.0f, 0x7FFFFFFF};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E) c = better(c, Cand{sel[j], sc[j], e});
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      Cand o{__shfl_xor(c.v, off, 64), __shfl_xor(c.s, off, 64), __shfl_xor(c.i, off, 64)};
-      c = better(c, o);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == c.i) sel[j] = -INFINITY;   // remove the winner
-    wsel[r] = c.s;
-    isel[r] = c.i;
-  }
-  if (lane == 0) {
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (r < k) sum = sum + wsel[r];
-    const float denom = sum + 1e-20f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (r < k) {
-        ids[(size_t)t * k + r] = isel[r];
-        rw[(size_t)t * k + r] = (wsel[r] / denom) * route_scale;
-      }
-    }
-  }
-  }
-  // ---- QDQ of the row: one 32-wide block per thread per iteration
+  if (threadIdx.x < 64)
+    select_token(t, M, E, k, route_scale, nparts, logits, gate_b, threadIdx.x, ids, rw, nullptr, nullptr);
+  if (M <= kSmallM) return;
   const int nb = H / 32;
-  for (int b = threadIdx.x; b < nb; b += 256) {
-    const uint16_t* src = x + (size_t)t * H + b * 32;
-    u32x4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 8 * i);
-    float v[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = bits_to_f32(raw[i][j] << 16);
-        v[8 * i + 2 * j + 1] = bits_to_f32(raw[i][j] & 0xFFFF0000u);
-      }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const int E8 = qdq_exponent(amax);
-    const float inv = exp2_neg(E8);
-    u32x4 out[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c0 = qdq_code(v[4 * i], inv), c1 = qdq_code(v[4 * i + 1], inv);
-      const uint32_t c2 = qdq_code(v[4 * i + 2], inv), c3 = qdq_code(v[4 * i + 3], inv);
-      out[i >> 2][i & 3] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(x_q + (size_t)t * H + b * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    x_s[(size_t)t * nb + b] = uint8_t(E8 + 127);
-  }
+  for (int b = threadIdx.x; b < nb; b += 256)
+    qdq_block32(x + (size_t)t * H + b * 32, x_q + (size_t)t * H + b * 32, x_s + (size_t)t * nb + b);
 }
 
 int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : kLargeParts; }
 
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          hipStream_t s) {
+                          uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
   if (M <= kSmallM) {
-    router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits);
+    router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits,
+                                                                                           x_q, x_s);
   } else {
     router_logits_tiled<<<dim3((M + 63) / 64, kLargeParts, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_w,
                                                                                             logits);

@@ -1,0 +1,171 @@
+// Per-token router selection and per-32 activation QDQ as device functions, shared by the separate
+// router kernels and the fused decode-width select + permute kernel, so that every path makes the same
+// decisions in the same fp32 order.
+//
+// Gate (DeepSeek-V4.1-Flash native-tensor page, section 2 "Gate"): scores sqrt(softplus(l)), top-k of
+// scores + bias (the bias only selects), the chosen scores normalised by their sum + 1e-20 and scaled
+// by the route scale. Activation QDQ (same section, "Quantized linear"): per 32 inputs, E8M0 scale
+// 2^ceil(log2(max(amax, 1e-4) / 448)) and E4M3 codes.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+// Partial logit planes per token: H / 512 at decode widths (H <= 8192), 4 above.
+constexpr int kMaxLogitParts = 16;
+
+// fp32 -> unsigned key with the same order (finite values; -0 and +0 both map to the key of +0, as
+// they compare equal). Every finite value maps above 0.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Maximum of a 64-bit value over the 64 lanes of the wave, returned to every lane (wave-uniform).
+// Inside each 16-lane row: DPP exchanges with the lane at xor 1 and xor 2 (quad permutes), then with the
+// mirrored lane in the 8-lane half and in the row, each step taking the larger value, so every lane
+// ends with its row's maximum; then the four row maxima are read as scalars.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#define MOE_DPP_MAX_STEP(ctrl)                                                                        \
+  {                                                                                                   \
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false);  \
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false); \
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;                                                   \
+    if (o > v) v = o;                                                                                 \
+  }
+  MOE_DPP_MAX_STEP(0xB1)    // quad_perm [1, 0, 3, 2]
+  MOE_DPP_MAX_STEP(0x4E)    // quad_perm [2, 3, 0, 1]
+  MOE_DPP_MAX_STEP(0x141)   // row_half_mirror
+  MOE_DPP_MAX_STEP(0x140)   // row_mirror
+#undef MOE_DPP_MAX_STEP
+  uint64_t m = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    if (o > m) m = o;
+  }
+  return m;
+}
+
+// One wave selects the experts of token t from the partial logit planes [nparts][M][E] (added in
+// ascending plane order). Lane 0 writes ids[t * k + r] and rw[t * k + r] (r = rank, descending
+// selection score); when sid is given, the ids to sid[t * k + r] too, and when emask is given (t < 64)
+// it sets bit t of emask[id] for each chosen expert. The k ids of a token are distinct. E <= 256, k <= 8.
+__device__ __forceinline__ void select_token(int t, int M, int E, int k, float route_scale, int nparts,
+                                             const float* __restrict__ logits, const float* __restrict__ gate_b,
+                                             int lane, int32_t* __restrict__ ids, float* __restrict__ rw,
+                                             int* sid, unsigned long long* emask) {
+  // scores and selection values: lane owns experts lane, lane + 64, ... Every partial logit load is
+  // issued before the first is used; the planes are then added in ascending order.
+  const size_t plane = (size_t)M * E;
+  float pv[4][kMaxLogitParts], bias[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    bias[j] = 0.0f;
+    if (e < E) {
+      const float* lp = logits + (size_t)t * E + e;
+#pragma unroll
+      for (int c = 0; c < kMaxLogitParts; ++c) pv[j][c] = c < nparts ? lp[c * plane] : 0.0f;
+      bias[j] = gate_b[e];
+    }
+  }
+  float sc[4];
+  uint32_t key[4];   // selection order as one unsigned key: ordered fp32 bits of the selection score
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    sc[j] = 0.0f;
+    key[j] = 0u;   // below every real candidate
+    if (e < E) {
+      float l = pv[j][0];
+#pragma unroll
+      for (int c = 1; c < kMaxLogitParts; ++c)
+        if (c < nparts) l = l + pv[j][c];
+      const float sp = l > 20.0f ? l : log1pf(expf(l));
+      sc[j] = sqrtf(sp);
+      key[j] = ordered_key(sc[j] + bias[j]);
+    }
+  }
+  // k rounds of a wave-wide maximum of (key, -expert id): the larger selection score wins, equal
+  // scores go to the lower expert id; the winner's lane then hands over its unbiased score
+  float wsel[8];
+  int isel[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    wsel[r] = 0.0f;
+    isel[r] = 0;
+    if (r >= k) continue;
+    uint64_t best = 0;   // (key << 32) | (0xFFFFFFFF - expert id)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t c = ((uint64_t)key[j] << 32) | (0xFFFFFFFFu - uint32_t(lane + 64 * j));
+      if (c > best) best = c;
+    }
+    best = wave_max_u64(best);
+    const int win = int(0xFFFFFFFFu - uint32_t(best));
+    const int jw = win >> 6;
+    float mine = sc[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (jw == j) mine = sc[j];
+    wsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), win & 63));
+    isel[r] = win;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == win) key[j] = 0u;   // remove the winner
+  }
+  if (lane == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < k) sum = sum + wsel[r];
+    const float denom = sum + 1e-20f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r < k) {
+        ids[(size_t)t * k + r] = isel[r];
+        rw[(size_t)t * k + r] = (wsel[r] / denom) * route_scale;
+        if (sid != nullptr) sid[t * k + r] = isel[r];
+        if (emask != nullptr) atomicOr(&emask[isel[r]], 1ull << t);
+      }
+    }
+  }
+}
+
+// QDQ of one 32-wide block of a bf16 row: 32 E4M3 codes to q (16-byte aligned) and the E8M0 byte to *s.
+__device__ __forceinline__ void qdq_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
+                                            uint8_t* __restrict__ s) {
+  u32x4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 8 * i);
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = bits_to_f32(raw[i][j] << 16);
+      v[8 * i + 2 * j + 1] = bits_to_f32(raw[i][j] & 0xFFFF0000u);
+    }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int E8 = qdq_exponent(amax);
+  const float inv = exp2_neg(E8);
+  u32x4 out[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c0 = qdq_code(v[4 * i], inv), c1 = qdq_code(v[4 * i + 1], inv);
+    const uint32_t c2 = qdq_code(v[4 * i + 2], inv), c3 = qdq_code(v[4 * i + 3], inv);
+    out[i >> 2][i & 3] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(q);
+  dst[0] = out[0];
+  dst[1] = out[1];
+  *s = uint8_t(E8 + 127);
+}
+
+}  // namespace moe

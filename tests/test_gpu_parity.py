@@ -468,3 +468,35 @@ def test_decode_path_is_batch_invariant():
     for M in (32, 64):
         assert np.array_equal(outs[M][0], outs[8][0]), f"routing of the first tokens changes with M={M}"
         assert np.array_equal(outs[M][1], outs[8][1]), f"outputs of the first tokens change with M={M}"
+
+
+@pytest.mark.parametrize("M", [1, 8, 63, 64, 65])
+def test_forward_routing_equals_route_and_permute_calls(M):
+    """moe_forward fuses the selection with the permutation at M <= 64; its ids and route weights equal
+    the separate moe_route call's bit for bit, at and around the switch."""
+    cfg, inp, d = cfg_inputs(2)
+    c = synth.get_config(2, M=M)
+    if M > cfg.M:
+        sub = dict(inp)
+        sub["x"] = np.concatenate([inp["x"], inp["x"][: M - cfg.M] ^ np.uint16(0x8000)])
+        xdev = dev_tensor(sub["x"])
+    else:
+        xdev = d["x"][:M]
+    dims = dims_of(c)
+    ws = m().workspace(dims, M)
+    ids = torch.empty((M, c.k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((M, c.k), dtype=torch.float32, device="cuda")
+    xq = torch.empty((M, c.H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, c.H // 32), dtype=torch.uint8, device="cuda")
+    m().moe_route(dims, xdev, d["gate_w"], d["gate_b"], ids, rw, xq, xs, ws)
+    out = torch.empty((M, c.H), dtype=torch.int16, device="cuda")
+    ids_f = torch.empty_like(ids)
+    rw_f = torch.empty_like(rw)
+    m().moe_forward(dims, xdev, d["gate_w"], d["gate_b"], packed_of(d), None, None, out, ids_f, rw_f, None,
+                    m().workspace(dims, M))
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_f)
+    assert torch.equal(rw.view(torch.int32), rw_f.view(torch.int32))
+    codes, sb, _ = O.act_qdq(F.bf16_from_bits(xdev.cpu().numpy().view(np.uint16)))
+    assert np.array_equal(xq.cpu().numpy(), codes)
+    assert np.array_equal(xs.cpu().numpy(), sb)
