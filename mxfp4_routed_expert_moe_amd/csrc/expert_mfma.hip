@@ -90,6 +90,12 @@ __device__ __forceinline__ void ring_barrier() {
   else static_assert(N == 0 || N == 8 || N == 16 || N == 10 || N == 14 || N == 20 || N == 28, "vmcnt immediate");
 }
 
+// Compile-time tags: every B fragment of the wave holds tile rows (kFull) or the tile may be partial.
+struct FullTag { static constexpr bool value = false; };
+struct PartialTag { static constexpr bool value = true; };
+constexpr FullTag kFull{};
+constexpr PartialTag kPartial{};
+
 // Fragments of one stage held in registers (double-buffered across stages).
 template <int WF>
 struct Frags {
@@ -251,16 +257,23 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
 #pragma unroll
   for (int b = 0; b < 4; ++b) brow_l[b] = 64 * wm + 16 * b + r16;
 
-  auto read_frags = [&](Frags<WF>& F, int s) {
+  // B fragments of this wave that hold a row of the tile (the last tile of an expert is partial):
+  // the others are neither read nor multiplied (wave-uniform)
+  const int nbv = min(4, max(0, (nrows - 64 * wm + 15) / 16));
+  // PART: the tile may be partial (checked per fragment); otherwise all four B fragments hold rows
+  auto read_frags = [&](Frags<WF>& F, int s, auto part) {
+    constexpr bool PART = decltype(part)::value;
     const Stage<WF, TN>& st = ring[s % kStages];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+      if (PART && b >= nbv) continue;
       const int t = brow_l[b];
       const int key = chunk_key<kStepK>(t);
       F.b0[b] = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * (g ^ key)]);
       F.b1[b] = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * ((4 + g) ^ key)]);
       F.bs[b] = st.as[t * 4 + g];
     }
+    if (PART && nbv == 0) return;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const int r = arow_l[a];
@@ -270,7 +283,8 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
       F.as[a] = st.ws[r * 4 + g];
     }
   };
-  auto mfmas = [&](const Frags<WF>& F) {
+  auto mfmas = [&](const Frags<WF>& F, auto part) {
+    constexpr bool PART = decltype(part)::value;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       i32x8 Af;
@@ -281,6 +295,7 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
                    (int)F.a1[a][0], (int)F.a1[a][1], (int)F.a1[a][2], (int)F.a1[a][3]};
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
+        if (PART && b >= nbv) continue;
         const i32x8 Bf = i32x8{(int)F.b0[b][0], (int)F.b0[b][1], (int)F.b0[b][2], (int)F.b0[b][3],
                                (int)F.b1[b][0], (int)F.b1[b][1], (int)F.b1[b][2], (int)F.b1[b][3]};
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[a][b], T::kFmt, kFmtFp8, 0, F.as[a],
@@ -294,8 +309,8 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     if (s + 2 < nk) ring_barrier<LPS>();
     else ring_barrier<0>();
     if (s + 3 < nk) issue(s + 3);
-    mfmas(cur);
-    read_frags(nxt, s + 1);
+    mfmas(cur, kFull);
+    read_frags(nxt, s + 1, kFull);
     // scheduling: one LDS read after each MFMA (the reads do not depend on the MFMAs)
 #pragma unroll
     for (int i = 0; i < (WF == W_MXFP4 ? 28 : 32); ++i) {
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     if (nk > 2) ring_barrier<2 * LPS>();   // stage 0 landed (stages 1, 2 in flight)
     else if (nk > 1) ring_barrier<LPS>();
     else ring_barrier<0>();
-    read_frags(F0, 0);
+    read_frags(F0, 0, kFull);
     int s = 0;
     for (; s + 2 < nk; s += 2) {   // pairs of steps keep the two register sets static
       step(F0, F1, s);
@@ -322,22 +337,28 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     }
     if (s + 1 < nk) {
       step(F0, F1, s);
-      mfmas(F1);
+      mfmas(F1, kFull);
     } else {
-      mfmas(F0);
+      mfmas(F0, kFull);
     }
   } else {
     // two waves per SIMD cover each other's LDS latency: one fragment set (fits 256 registers)
+    // (a partial tile, the last one of an expert, runs its own copy of the loop that skips the empty
+    // B fragments; full tiles run a copy without the checks)
     Frags<WF> F;
     issue(0);
     if (nk > 1) issue(1);
-    for (int s = 0; s < nk; ++s) {
-      if (s + 1 < nk) ring_barrier<LPS>();   // stage s landed (stage s + 1 may still be in flight)
-      else ring_barrier<0>();
-      if (s + 2 < nk) issue(s + 2);           // into the slot computed at s - 1: every wave is past it
-      read_frags(F, s);
-      mfmas(F);
-    }
+    auto kloop = [&](auto part) {
+      for (int s = 0; s < nk; ++s) {
+        if (s + 1 < nk) ring_barrier<LPS>();   // stage s landed (stage s + 1 may still be in flight)
+        else ring_barrier<0>();
+        if (s + 2 < nk) issue(s + 2);           // into the slot computed at s - 1: every wave is past it
+        read_frags(F, s, part);
+        mfmas(F, part);
+      }
+    };
+    if (nbv == 4) kloop(kFull);
+    else kloop(kPartial);
   }
 
   // ---- epilogue: lane holds weight rows 4g..4g+3 of each A fragment for activation row r16 of each B
