@@ -224,14 +224,27 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     const int gc = (lane % 8) ^ chunk_key<kStepK>(t);
     asrc[i] = p.act_q + (size_t)act_row(t) * K + gc * 16;
   }
+  // weight scales: 4 bytes per row per stage; stage-major MXFP4 scales put a stage's rows side by side
   const uint8_t* wssrc;
+  const size_t ws_step = (WF == W_MXFP4 && p.s_stage_major) ? (size_t)p.N * 4 : 4;
   {
     const int r = wave * 64 + lane;
     const uint8_t* sb = (GEMM1 && r >= TN / 2) ? p.sb : p.sa;
-    wssrc = (WF == W_MXFP4) ? sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * KB
-                            : sb + (size_t)(grow_of(r) / 32) * KB;
+    if (WF == W_MXFP4)
+      wssrc = sb + (size_t)e * p.s_expert_stride + (size_t)grow_of(r) * (p.s_stage_major ? 4 : KB);
+    else
+      wssrc = sb + (size_t)(grow_of(r) / 32) * KB;
   }
-  const uint8_t* assrc = p.act_s + (size_t)act_row(wave * kARows + (lane % kARows)) * KB;
+  // activation scales of the wave's kARows rows: 4 bytes per row per stage (stage-major: side by side)
+  const uint8_t* assrc;
+  size_t as_step = 4;
+  if (p.a_stage_major) {
+    const int t = wave * kARows + (lane % kARows);
+    assrc = p.act_s + (size_t)(row0 + (t < nrows ? t : 0)) * 4;
+    as_step = (size_t)p.M * p.k * 4;
+  } else {
+    assrc = p.act_s + (size_t)act_row(wave * kARows + (lane % kARows)) * KB;
+  }
   auto issue = [&](int s) {
     Stage<WF, TN>& st = ring[s % kStages];
     const int k0 = s * kStepK;
@@ -240,8 +253,8 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
       dma16(wsrc[i] + (WF == W_MXFP4 ? k0 / 2 : k0), &st.w[(wave * 64 + i * kWRows) * kRB]);
 #pragma unroll
     for (int i = 0; i < kAInstr; ++i) dma16(asrc[i] + k0, &st.a[(wave * kARows + i * 8) * kStepK]);
-    dma4(wssrc + k0 / 32, &st.ws[wave * 64 * 4]);
-    if (lane < kARows) dma4(assrc + k0 / 32, &st.as[wave * kARows * 4]);
+    dma4(wssrc + (size_t)s * ws_step, &st.ws[wave * 64 * 4]);
+    if (lane < kARows) dma4(assrc + (size_t)s * as_step, &st.as[wave * kARows * 4]);
   };
 
   f32x4 acc[8][4];
@@ -398,7 +411,12 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
             for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
             *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + col0 + 16 * half + 4 * g) = packed;
           }
-          if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + col0 / 32] = uint8_t(E8 + 127);
+          if (g == 0) {
+            const size_t at = p.h_s_stage_major
+                                  ? ((size_t)(col0 / 128) * p.M * p.k + pos) * 4 + (col0 / 32) % 4
+                                  : (size_t)pos * (p.N / 32) + col0 / 32;
+            p.h_s[at] = uint8_t(E8 + 127);
+          }
         }
       }
     } else {
@@ -414,6 +432,43 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
       }
     }
   }
+}
+
+// One block per 64 rows of one matrix: the rows' scale bytes go through LDS (coalesced dword reads
+// along the rows, coalesced dword writes along the stage-major rows).
+__global__ __launch_bounds__(256) void scales_stage_major_kernel(int N, int KB, const uint8_t* __restrict__ s,
+                                                                 uint8_t* __restrict__ S) {
+  __shared__ uint32_t t[64][65];
+  const int q4 = KB / 4;   // stages (dwords per row), at most 64
+  const int n0 = blockIdx.x * 64;
+  const size_t m = blockIdx.y;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(s + (m * N + n0) * (size_t)KB);
+  for (int i = threadIdx.x; i < 64 * q4; i += 256) t[i / q4][i % q4] = src[i];
+  __syncthreads();
+  uint32_t* dst = reinterpret_cast<uint32_t*>(S + m * N * (size_t)KB);
+  for (int i = threadIdx.x; i < 64 * q4; i += 256) {
+    const int q = i / 64, r = i % 64;
+    dst[(size_t)q * N + n0 + r] = t[r][q];
+  }
+}
+
+void launch_scales_stage_major(int mats, int N, int K, const uint8_t* s, uint8_t* S, hipStream_t st) {
+  scales_stage_major_kernel<<<dim3(N / 64, mats), dim3(256), 0, st>>>(N, K / 32, s, S);
+}
+
+// Thread per (stage q, sorted position): one dword gathered from the token's scale row.
+__global__ __launch_bounds__(256) void gather_act_scales_kernel(int P, int k, int q4, const int32_t* __restrict__ pairs,
+                                                                const uint8_t* __restrict__ x_s, uint8_t* __restrict__ out) {
+  const int pos = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
+  if (pos >= P) return;
+  const int t = pairs[pos] / k;
+  reinterpret_cast<uint32_t*>(out)[(size_t)q * P + pos] =
+      reinterpret_cast<const uint32_t*>(x_s + (size_t)t * q4 * 4)[q];
+}
+
+void launch_gather_act_scales(int P, int k, int K, const int32_t* pairs, const uint8_t* x_s, uint8_t* out,
+                              hipStream_t st) {
+  gather_act_scales_kernel<<<dim3((P + 255) / 256, K / 128), dim3(256), 0, st>>>(P, k, K / 128, pairs, x_s, out);
 }
 
 int mfma_max_tiles(int P, int E) { return (P + kTileM - 1) / kTileM + (P < E ? P : E); }

@@ -60,6 +60,13 @@ struct GemmProblem {
   // outputs
   uint8_t* h_q; uint8_t* h_s;  // GEMM1: QDQ'd h codes [rows, N] and scales [rows, N/32]
   uint16_t* out;               // GEMM2: bf16 [*, N]; row = pair id (routed) or token (dense)
+  // MXFP4 scales in the stage-major copy made by launch_scales_stage_major (block-scaled MFMA kernels
+  // only): [E][K/128][N][4] instead of [E][N][K/32]
+  int s_stage_major;
+  // activation scales stage-major by sorted position, [K/128][M*k][4] (routed block-scaled MFMA only)
+  int a_stage_major;
+  // GEMM1 output scales h_s written stage-major, [N/128][M*k][4], for a GEMM2 with a_stage_major
+  int h_s_stage_major;
 };
 // GEMM1: g = w1 x, u = w3 x -> bf16 -> SwiGLU (x rw) -> bf16 -> QDQ per 32 -> h_q, h_s
 void launch_gemm1_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
@@ -77,6 +84,14 @@ int mfma_max_tiles(int P, int E);
 void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile_e, int32_t* tile_r0, int32_t* info,
                      hipStream_t s);
 // Same problems as the *_small launchers (MXFP4 or FP8 weights only); routed problems take the tile list.
+// Stage-major copy of MXFP4 E8M0 scales for the block-scaled MFMA kernels: mats matrices s[m][N][K/32]
+// -> S[m][K/128][N][4], so the 4 scale bytes of one 128-wide K step of consecutive rows are contiguous
+// (one stage's scales of 64 rows are 256 contiguous bytes instead of 64 strided dwords).
+void launch_scales_stage_major(int mats, int N, int K, const uint8_t* s, uint8_t* S, hipStream_t st);
+// Activation scales of the P = M*k sorted pairs, stage-major: out[K/128][P][4] from x_s[token][K/32],
+// token = pairs[pos] / k.
+void launch_gather_act_scales(int P, int k, int K, const int32_t* pairs, const uint8_t* x_s, uint8_t* out,
+                              hipStream_t st);
 void launch_gemm1_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
                        const int32_t* tile_r0, const int32_t* info, hipStream_t s);
 void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,

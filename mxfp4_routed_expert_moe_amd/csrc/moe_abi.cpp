@@ -16,7 +16,7 @@ using moe::GemmProblem;
 
 struct WsLayout {
   size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
-      sh_q, sh_s, sh_out;
+      sh_q, sh_s, sh_out, scales, xs_sm;
   size_t total;
 };
 
@@ -53,6 +53,10 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.sh_q = take(m * I);
   L.sh_s = take(m * I / 32);
   L.sh_out = take(m * H * 2);
+  // stage-major copies of the routed w1, w3 and w2 scales for the prefill-width GEMMs
+  L.scales = take(m * k >= 32 * E ? 3 * E * I * H / 32 : 0);
+  // the activation scales of the sorted pairs, stage-major (prefill width)
+  L.xs_sm = take(m * k >= 32 * E ? m * k * H / 32 : 0);
   L.total = off;
   return L;
 }
@@ -121,6 +125,9 @@ struct TileMap {
   const int32_t* tile_e = nullptr;
   const int32_t* tile_r0 = nullptr;
   const int32_t* info = nullptr;
+  uint8_t* scales = nullptr;   // workspace room for the stage-major w1, w3, w2 scales
+  uint8_t* xs_sm = nullptr;    // workspace room for the stage-major activation scales of GEMM1
+  bool act_sm = false;         // GEMM1 reads stage-major activation scales and writes h_s stage-major
 };
 
 TileMap make_tile_map(const moe_dims* d, int M, const int32_t* offsets, void* ws, hipStream_t s) {
@@ -134,6 +141,8 @@ TileMap make_tile_map(const moe_dims* d, int M, const int32_t* offsets, void* ws
   t.tile_e = te;
   t.tile_r0 = tr;
   t.info = ti;
+  t.scales = at<uint8_t>(ws, L.scales);
+  t.xs_sm = at<uint8_t>(ws, L.xs_sm);
   return t;
 }
 void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, const float* gb, int32_t* ids,
@@ -168,7 +177,18 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   p.N = I; p.K = H;
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = hq; p.h_s = hs;
-  if (routed_mfma(d, M, packed)) moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+  if (routed_mfma(d, M, packed)) {
+    uint8_t* s1 = tm.scales;
+    uint8_t* s3 = s1 + (size_t)E * I * (H / 32);
+    moe::launch_scales_stage_major(E, I, H, packed->s1, s1, s);
+    moe::launch_scales_stage_major(E, I, H, packed->s3, s3, s);
+    p.sa = s1; p.sb = s3; p.s_stage_major = 1;
+    if (tm.act_sm) {   // h stays in the workspace: both GEMMs take their activation scales stage-major
+      moe::launch_gather_act_scales(M * k, k, H, pairs, xs, tm.xs_sm, s);
+      p.act_s = tm.xs_sm; p.a_stage_major = 1; p.h_s_stage_major = 1;
+    }
+    moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+  }
   else if (packed) moe::launch_gemm1_stream(f, p, max_active, s);
   else moe::launch_gemm1_small(f, p, max_active, s);
 }
@@ -195,16 +215,28 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.N = H; q.K = I;
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot;
-  if (routed_mfma(d, M, packed)) moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+  if (routed_mfma(d, M, packed)) {
+    uint8_t* s2 = tm.scales + 2 * (size_t)E * I * (H / 32);
+    moe::launch_scales_stage_major(E, H, I, packed->s2, s2, s);
+    q.sa = s2; q.s_stage_major = 1;
+    q.a_stage_major = tm.act_sm ? 1 : 0;
+    moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+  }
   else if (packed) moe::launch_gemm2_stream(f, q, max_active, s);
   else moe::launch_gemm2_small(f, q, max_active, s);
 }
 
+// h_internal: h_q / h_s are workspace buffers no caller reads, so the prefill GEMMs may keep h_s in
+// their own stage-major layout.
 void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
                    const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
-                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, void* ws, hipStream_t s) {
+                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, bool h_internal, void* ws,
+                   hipStream_t s) {
   TileMap tm;
-  if (routed_mfma(d, M, packed)) tm = make_tile_map(d, M, offsets, ws, s);
+  if (routed_mfma(d, M, packed)) {
+    tm = make_tile_map(d, M, offsets, ws, s);
+    tm.act_sm = h_internal;
+  }
   do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, tm, s);
   do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, tm, s);
 }
@@ -287,11 +319,12 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
   if (h_q != nullptr && !al(h_q, 16)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   const WsLayout L = ws_layout(dims, M);
-  if (h_q == nullptr) {
+  const bool h_internal = h_q == nullptr;
+  if (h_internal) {
     h_q = at<uint8_t>(ws, L.h_q);
     h_s = at<uint8_t>(ws, L.h_s);
   }
-  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s, ws,
+  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s, h_internal, ws,
                 static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -393,7 +426,7 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
   }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, at<uint8_t>(ws, L.h_q),
-                at<uint8_t>(ws, L.h_s), ws, s);
+                at<uint8_t>(ws, L.h_s), true, ws, s);
   uint16_t* sh_out = nullptr;
   if (shared != nullptr) {
     sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
