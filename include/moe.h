@@ -70,6 +70,10 @@ typedef struct {
   const uint8_t* s3; /* [E, I, H/32]                  */
   const uint8_t* w2; /* [E, H, I/2]  down projection  */
   const uint8_t* s2; /* [E, H, I/32]                  */
+  /* Optional (NULL = none): the output of moe_prepare_mxfp4_scales for these scales. The prefill-width
+   * kernels read the scales from it; without it every prefill-width call re-lays them out in the
+   * workspace. */
+  const uint8_t* stage_scales;
 } moe_mxfp4_experts;
 
 /* Routed experts expanded to bf16 (section 4 "expanded weights": exactly code * 2^(b-127)). */
@@ -159,6 +163,18 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                        const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
                        uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Bytes of moe_prepare_mxfp4_scales output: 3 * E * I * H / 32 (0 if dims are invalid). */
+size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims);
+
+/* One-time re-layout of the routed experts' E8M0 scales for the prefill-width (block-scaled matrix
+ * core) kernels, which read one 128-wide K step of many rows at a time. For each of s1, s3, s2 in that
+ * order (matrix m = [E, N, K/32]: N = I, K = H for s1 and s3; N = H, K = I for s2), out holds
+ * [E, K/128, N, 4] with out[e][q][n][b] = s[e][n][4q + b]. The scales are constant, so this is done
+ * once (e.g. when the weights are loaded); the values are unchanged, only their order. out: device,
+ * 16-byte aligned, moe_mxfp4_stage_scales_bytes(dims) bytes, owned by the caller. w's weight
+ * pointers are not read (w->stage_scales is ignored). */
+moe_status moe_prepare_mxfp4_scales(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream);
 
 /* Expand one packed MXFP4 matrix (or a stack of them) to bf16: w uint8 [rows, cols/2], s uint8
  * [rows, cols/32] -> out bf16 [rows, cols], exactly code * 2^(b-127) (section 4 "expanded weights").

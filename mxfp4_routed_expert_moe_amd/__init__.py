@@ -19,6 +19,7 @@ __all__ = [
     "LIB_PATH", "MoeError", "Dims", "MXFP4Experts", "BF16Experts", "FP8Expert", "lib",
     "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute", "moe_expert_ffn",
     "moe_expert_gemm1", "moe_expert_gemm2", "moe_shared_expert", "moe_combine", "moe_forward", "moe_expand_mxfp4", "workspace",
+    "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -41,7 +42,7 @@ class _Dims(ctypes.Structure):
 
 
 class _MXFP4(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")]
 
 
 class _BF16(ctypes.Structure):
@@ -80,6 +81,10 @@ lib.moe_combine.restype = _I32
 lib.moe_forward.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
                             ctypes.POINTER(_FP8), _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_forward.restype = _I32
+lib.moe_mxfp4_stage_scales_bytes.argtypes = [ctypes.POINTER(_Dims)]
+lib.moe_mxfp4_stage_scales_bytes.restype = _SZ
+lib.moe_prepare_mxfp4_scales.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
+lib.moe_prepare_mxfp4_scales.restype = _I32
 lib.moe_expand_mxfp4.argtypes = [ctypes.c_int64, _I32, _P, _P, _P, _P]
 lib.moe_expand_mxfp4.restype = _I32
 
@@ -98,16 +103,18 @@ class Dims:
 
 @dataclass
 class MXFP4Experts:
-    """Packed routed experts: w1/w3 uint8 [E, I, H/2], s1/s3 [E, I, H/32], w2 [E, H, I/2], s2 [E, H, I/32]."""
+    """Packed routed experts: w1/w3 uint8 [E, I, H/2], s1/s3 [E, I, H/32], w2 [E, H, I/2], s2 [E, H, I/32];
+    optionally the moe_prepare_mxfp4_scales output of these scales (uint8, 16-byte aligned)."""
     w1: torch.Tensor
     s1: torch.Tensor
     w3: torch.Tensor
     s3: torch.Tensor
     w2: torch.Tensor
     s2: torch.Tensor
+    stage_scales: torch.Tensor | None = None
 
     def c(self) -> _MXFP4:
-        return _MXFP4(*(_ptr(getattr(self, n), torch.uint8) for n in ("w1", "s1", "w3", "s3", "w2", "s2")))
+        return _MXFP4(*(_ptr(getattr(self, n), torch.uint8) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")))
 
 
 @dataclass
@@ -271,3 +278,20 @@ def moe_expand_mxfp4(w, s, out, stream=None):
     st = lib.moe_expand_mxfp4(rows, cols, _ptr(w, torch.uint8), _ptr(s, torch.uint8), _ptr(out, _BF),
                               _stream(stream))
     _check(st, "moe_expand_mxfp4")
+
+
+def moe_mxfp4_stage_scales_bytes(dims: Dims) -> int:
+    return int(lib.moe_mxfp4_stage_scales_bytes(ctypes.byref(dims.c())))
+
+
+def moe_prepare_mxfp4_scales(dims: Dims, packed: MXFP4Experts, out=None, stream=None) -> torch.Tensor:
+    """The stage-major copy of packed's s1, s3, s2 (into out, or a new uint8 tensor on their device)."""
+    n = moe_mxfp4_stage_scales_bytes(dims)
+    if n == 0:
+        raise MoeError("invalid dims for stage scales")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=packed.s1.device)
+    st = lib.moe_prepare_mxfp4_scales(ctypes.byref(dims.c()), ctypes.byref(packed.c()), _ptr(out, torch.uint8),
+                                      _stream(stream))
+    _check(st, "moe_prepare_mxfp4_scales")
+    return out

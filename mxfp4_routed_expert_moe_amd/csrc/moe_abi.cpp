@@ -97,7 +97,14 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
 moe_status check_packed(const moe_mxfp4_experts* w) {
   if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16))
     return MOE_ERR_INVALID_ARG;
+  if (w->stage_scales != nullptr && !al(w->stage_scales, 16)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// Offsets of the s1, s3, s2 stage-major copies inside moe_prepare_mxfp4_scales output (and the
+// workspace copy).
+inline size_t stage_scales_off(const moe_dims* d, int which) {
+  return (size_t)which * d->num_experts * (size_t)d->inter * (d->hidden / 32);
 }
 
 moe_status check_decoded(const moe_bf16_experts* w) {
@@ -178,11 +185,17 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
   p.act_q = xq; p.act_s = xs; p.act_by_token = 1;
   p.h_q = hq; p.h_s = hs;
   if (routed_mfma(d, M, packed)) {
-    uint8_t* s1 = tm.scales;
-    uint8_t* s3 = s1 + (size_t)E * I * (H / 32);
-    moe::launch_scales_stage_major(E, I, H, packed->s1, s1, s);
-    moe::launch_scales_stage_major(E, I, H, packed->s3, s3, s);
-    p.sa = s1; p.sb = s3; p.s_stage_major = 1;
+    if (packed->stage_scales != nullptr) {
+      p.sa = packed->stage_scales + stage_scales_off(d, 0);
+      p.sb = packed->stage_scales + stage_scales_off(d, 1);
+    } else {
+      uint8_t* s1 = tm.scales + stage_scales_off(d, 0);
+      uint8_t* s3 = tm.scales + stage_scales_off(d, 1);
+      moe::launch_scales_stage_major(E, I, H, packed->s1, s1, s);
+      moe::launch_scales_stage_major(E, I, H, packed->s3, s3, s);
+      p.sa = s1; p.sb = s3;
+    }
+    p.s_stage_major = 1;
     if (tm.act_sm) {   // h stays in the workspace: both GEMMs take their activation scales stage-major
       moe::launch_gather_act_scales(M * k, k, H, pairs, xs, tm.xs_sm, s);
       p.act_s = tm.xs_sm; p.a_stage_major = 1; p.h_s_stage_major = 1;
@@ -216,9 +229,14 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot;
   if (routed_mfma(d, M, packed)) {
-    uint8_t* s2 = tm.scales + 2 * (size_t)E * I * (H / 32);
-    moe::launch_scales_stage_major(E, H, I, packed->s2, s2, s);
-    q.sa = s2; q.s_stage_major = 1;
+    if (packed->stage_scales != nullptr) {
+      q.sa = packed->stage_scales + stage_scales_off(d, 2);
+    } else {
+      uint8_t* s2 = tm.scales + stage_scales_off(d, 2);
+      moe::launch_scales_stage_major(E, H, I, packed->s2, s2, s);
+      q.sa = s2;
+    }
+    q.s_stage_major = 1;
     q.a_stage_major = tm.act_sm ? 1 : 0;
     moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   }
@@ -433,6 +451,22 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
     do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, s);
   }
   moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+  return launched();
+}
+
+size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims) {
+  if (check_dims(dims, 0) != MOE_OK) return 0;
+  return stage_scales_off(dims, 3);
+}
+
+moe_status moe_prepare_mxfp4_scales(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream) {
+  MOE_TRY(check_dims(dims, 0));
+  if (!w || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = dims->num_experts, H = dims->hidden, I = dims->inter;
+  moe::launch_scales_stage_major(E, I, H, w->s1, out + stage_scales_off(dims, 0), s);
+  moe::launch_scales_stage_major(E, I, H, w->s3, out + stage_scales_off(dims, 1), s);
+  moe::launch_scales_stage_major(E, H, I, w->s2, out + stage_scales_off(dims, 2), s);
   return launched();
 }
 

@@ -39,6 +39,10 @@ class Six(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
 
 
+class Packed(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")]
+
+
 class Three(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "w3", "w2")]
 
@@ -93,10 +97,10 @@ def _forward(lib, dims, M, x=FAKE, gw=FAKE, gb=FAKE, packed=True, decoded=False,
              ws_bytes=1 << 40, shared_out=None):
     f = lib.moe_forward
     f.restype = ctypes.c_int32
-    if isinstance(packed, Six):
+    if isinstance(packed, Packed):
         pk = ctypes.byref(packed)
     else:
-        pk = ctypes.byref(Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)) if packed else None
+        pk = ctypes.byref(Packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)) if packed else None
     dc = ctypes.byref(Three(FAKE, FAKE, FAKE)) if decoded else None
     sh = ctypes.byref(shared) if shared is not None else None
     return f(ctypes.byref(dims), ctypes.c_int32(M), ctypes.c_void_p(x), ctypes.c_void_p(gw), ctypes.c_void_p(gb), pk,
@@ -117,7 +121,8 @@ def test_forward_refuses_before_launch(lib):
     assert _forward(lib, d, 8, ws_bytes=1024) == WORKSPACE               # workspace too small
     assert _forward(lib, d, 8, shared=Six(FAKE, FAKE, FAKE, 0, FAKE, FAKE)) == INVALID   # partial shared set
     assert _forward(lib, d, 8, shared_out=FAKE) == INVALID               # shared_out without a shared expert
-    assert _forward(lib, d, 8, packed=Six(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE)) == INVALID   # misaligned scales
+    assert _forward(lib, d, 8, packed=Packed(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None)) == INVALID   # misaligned scales
+    assert _forward(lib, d, 8, packed=Packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8)) == INVALID   # misaligned copy
     assert _forward(lib, d, 8, shared=Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8)) == INVALID  # misaligned scales
     assert _forward(lib, Dims(128, 5120, 2304, 9, 1.5), 8) == UNSUPPORTED
     assert _forward(lib, Dims(512, 5120, 2304, 6, 1.5), 8) == UNSUPPORTED
@@ -158,3 +163,19 @@ def test_workspace_never_shrinks_as_m_grows(lib):
             w = f(ctypes.byref(d), M)
             assert w >= prev, (M, w, prev)
             prev = w
+
+
+def test_stage_scales_size_and_refusals(lib):
+    f = lib.moe_mxfp4_stage_scales_bytes
+    f.argtypes = [ctypes.POINTER(Dims)]
+    f.restype = ctypes.c_size_t
+    assert f(ctypes.byref(big())) == 3 * 128 * 2304 * 5120 // 32
+    assert f(ctypes.byref(Dims(128, 5000, 2304, 6, 1.5))) == 0
+    prep = lib.moe_prepare_mxfp4_scales
+    prep.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Packed), ctypes.c_void_p, ctypes.c_void_p]
+    prep.restype = ctypes.c_int32
+    ok = Packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert prep(ctypes.byref(big()), None, FAKE, None) == INVALID
+    assert prep(ctypes.byref(big()), ctypes.byref(ok), FAKE + 4, None) == INVALID
+    assert prep(ctypes.byref(big()), ctypes.byref(Packed(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None)), FAKE, None) == INVALID
+    assert prep(ctypes.byref(Dims(128, 5056, 2304, 6, 1.5)), ctypes.byref(ok), FAKE, None) == UNSUPPORTED

@@ -500,3 +500,35 @@ def test_forward_routing_equals_route_and_permute_calls(M):
     codes, sb, _ = O.act_qdq(F.bf16_from_bits(xdev.cpu().numpy().view(np.uint16)))
     assert np.array_equal(xq.cpu().numpy(), codes)
     assert np.array_equal(xs.cpu().numpy(), sb)
+
+
+def test_prepare_mxfp4_scales_layout():
+    """moe_prepare_mxfp4_scales re-lays out s1, s3, s2 as [E, K/128, N, 4] (the same bytes, checked
+    against a host transpose of the scale tensors)."""
+    cfg, inp, d = cfg_inputs(0, M=300, H=512, I=384, E=8, k=2)
+    out = m().moe_prepare_mxfp4_scales(dims_of(cfg), packed_of(d))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    parts = []
+    for name, N, K in (("s1", cfg.I, cfg.H), ("s3", cfg.I, cfg.H), ("s2", cfg.H, cfg.I)):
+        s = inp[name].reshape(cfg.E, N, K // 128, 4)
+        parts.append(np.ascontiguousarray(s.transpose(0, 2, 1, 3)).ravel())
+    assert got.size == m().moe_mxfp4_stage_scales_bytes(dims_of(cfg))
+    assert np.array_equal(got, np.concatenate(parts))
+
+
+@pytest.mark.parametrize("over", [dict(M=1000, H=512, I=256, E=8, k=2), dict(M=37, H=512, I=256, E=8, k=2)],
+                         ids=["prefill_width", "decode_width"])
+def test_forward_with_prepared_scales_is_identical(over):
+    """Passing the prepared stage-major scales changes where the prefill kernels read them, not the
+    result: outputs equal the call without them bit for bit (decode width ignores them)."""
+    cfg, inp, d = cfg_inputs(0, **over)
+    a = forward(cfg, d)
+    pk = packed_of(d)
+    pk.stage_scales = m().moe_prepare_mxfp4_scales(dims_of(cfg), pk)
+    dims = dims_of(cfg)
+    ws = m().workspace(dims, cfg.M)
+    out = torch.empty((cfg.M, cfg.H), dtype=torch.int16, device="cuda")
+    m().moe_forward(dims, d["x"], d["gate_w"], d["gate_b"], pk, None, None, out, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a["out_bits"])
