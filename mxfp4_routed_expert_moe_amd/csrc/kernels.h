@@ -15,10 +15,11 @@ namespace moe {
 constexpr int kRouterSmallM = 64;
 // fp32 logits of the raw bf16 activations against the fp32 gate weight [E, H], as
 // router_logit_parts(M, H) partial planes [parts, M, E] (summed in order by the select kernel).
-// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise).
+// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise); above, it first splits the gate into
+// gate_planes (3 * E * H bf16 of scratch).
 int router_logit_parts(int M, int H);
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, hipStream_t s);
+                          uint8_t* x_q, uint8_t* x_s, uint16_t* gate_planes, hipStream_t s);
 // sqrt(softplus) scores, biased top-k, normalised route weights; at M > kRouterSmallM also the
 // per-32 E4M3 QDQ of x.
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,

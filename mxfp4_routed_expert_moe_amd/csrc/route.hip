@@ -8,9 +8,9 @@
 //
 // Fixed fp32 orders (recorded so routing is reproducible): each logit is accumulated in fp32 as
 // strided partial sums (small M: per 512-wide chunk of H, 64 lanes x an 8-FMA chain, then a
-// butterfly, then the chunks added in ascending order; large M: per quarter of H, 32-wide FMA chains
-// summed into a running total, then the quarters added in ascending order); the normalising sum adds
-// the k weights in slot order.
+// butterfly, then the chunks added in ascending order; large M: per quarter of H, the bf16 matrix
+// cores' 32-wide K steps in ascending order, three exact split-gate products per step, then the
+// quarters added in ascending order); the normalising sum adds the k weights in slot order.
 #include "kernels.h"
 #include "moe_device.h"
 #include "route_device.h"
@@ -87,85 +87,90 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
   }
 }
 
-// Larger M: a block computes 64 tokens x 128 experts over one quarter of H (the quarters are added in
-// ascending order by the select kernel). Per 32-column chunk, x (transposed, fp32) and the gate tile
-// (transposed) sit in LDS; thread (tg, eg) owns tokens 8 tg .. 8 tg + 7 and experts 4 eg .. 4 eg + 3,
-// reads two float4 of x and one float4 of the gate per column, and runs 32 FMA chains. Each chunk's
-// 32-term chain is added to a running fp32 total.
+// Larger M, on the bf16 matrix cores. The fp32 gate is first split into three bf16 planes whose sum is
+// exactly the gate (hi = the top 8 significand bits, mid = the next 8 of the remainder, lo = the rest,
+// which has at most 8 bits): every product x * part is exact in fp32 (bf16 x bf16), so only the fp32
+// accumulation rounds, as in the vector path.
 constexpr int kLargeParts = 4;
 
-__global__ __launch_bounds__(256) void router_logits_tiled(int M, int H, int E, const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ gate_w,
-                                                           float* __restrict__ part) {
-  __shared__ __align__(16) float xs[32][64];
-  __shared__ __align__(16) float ws[32][128];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.z * 128;
+__global__ __launch_bounds__(256) void gate_split_kernel(size_t n, const float* __restrict__ gate,
+                                                         uint16_t* __restrict__ planes) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const float g = gate[i];
+    const uint32_t hi = __float_as_uint(g) & 0xFFFF0000u;
+    const float r1 = g - __uint_as_float(hi);                     // exact: the low 16 significand bits
+    const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(mid);                    // exact, at most 8 significant bits
+    planes[i] = uint16_t(hi >> 16);
+    planes[n + i] = uint16_t(mid >> 16);
+    planes[2 * n + i] = uint16_t(__float_as_uint(r2) >> 16);
+  }
+}
+
+// Block: 64 tokens x 128 experts over one quarter of H (the quarters are added in ascending order by the
+// select kernel). Wave w takes experts 32 w .. 32 w + 31 (two 16-wide B tiles) for all 64 tokens (four A
+// tiles). Per 32-wide K step, in ascending order: for each tile the hi, mid and lo products
+// (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column l % 16 of B, inputs
+// 8 (l / 16) .. + 7 of the step; the result (4 (l / 16) + v, l % 16) is accumulator v of lane l).
+__global__ __launch_bounds__(256) void router_logits_mfma(int M, int H, int E, const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ gp, float* __restrict__ part) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.z * 128 + 32 * wave;
   const int hq = H / kLargeParts, hbeg = blockIdx.y * hq;
-  const int tg = tid >> 5, eg = tid & 31;
-  float acc[8][4];
+  const size_t plane = (size_t)E * H;
+  const uint16_t* xr[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int a = 0; a < 4; ++a) xr[a] = x + (size_t)min(t0 + 16 * a + r16, M - 1) * H + hbeg + 8 * g;
+  const uint16_t* gr[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int h0 = hbeg; h0 < hbeg + hq; h0 += 32) {
-    {  // x tile: 64 tokens x 32 columns; thread loads 8 columns of one token
-      const int r = tid >> 2, c = (tid & 3) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t0 + r < M) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * H + h0 + c);
+  for (int b = 0; b < 2; ++b) gr[b] = gp + (size_t)min(e0 + 16 * b + r16, E - 1) * H + hbeg + 8 * g;
+  f32x4 acc[4][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xs[c + 2 * j][r] = bits_to_f32(v[j] << 16);
-        xs[c + 2 * j + 1][r] = bits_to_f32(v[j] & 0xFFFF0000u);
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int h, u32x4 (&A)[4], u32x4 (&B)[2][3]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) A[a] = *reinterpret_cast<const u32x4*>(xr[a] + h);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) B[b][q] = *reinterpret_cast<const u32x4*>(gr[b] + q * plane + h);
+  };
+  u32x4 A[4], B[2][3];
+  load(0, A, B);
+  for (int h = 0; h < hq; h += 32) {
+    u32x4 An[4], Bn[2][3];
+    if (h + 32 < hq) load(h + 32, An, Bn);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[a]),
+                                                             __builtin_bit_cast(bf16x8, B[b][q]), acc[a][b], 0, 0, 0);
+    if (h + 32 < hq) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) A[a] = An[a];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) B[b][q] = Bn[b][q];
+    }
+  }
+  float* out = part + (size_t)blockIdx.y * M * E;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int e = e0 + 16 * b + r16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 16 * a + 4 * g + v;
+        if (t < M && e < E) out[(size_t)t * E + e] = acc[a][b][v];
       }
     }
-    {  // gate tile: 128 experts x 32 columns; thread loads 16 columns of one expert
-      const int r = tid >> 1, c = (tid & 1) * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e0 + r < E) w = *reinterpret_cast<const float4*>(gate_w + (size_t)(e0 + r) * H + h0 + c + 4 * q);
-        ws[c + 4 * q][r] = w.x;
-        ws[c + 4 * q + 1][r] = w.y;
-        ws[c + 4 * q + 2][r] = w.z;
-        ws[c + 4 * q + 3][r] = w.w;
-      }
-    }
-    __syncthreads();
-    float p[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[i][j] = 0.0f;
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float4 xa = *reinterpret_cast<const float4*>(&xs[kk][8 * tg]);
-      const float4 xb = *reinterpret_cast<const float4*>(&xs[kk][8 * tg + 4]);
-      const float4 wv = *reinterpret_cast<const float4*>(&ws[kk][4 * eg]);
-      const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[i][j] = __builtin_fmaf(xv[i], wr[j], p[i][j]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] += p[i][j];
-    __syncthreads();
-  }
-  const size_t plane = (size_t)M * E;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + 8 * tg + i;
-    if (t >= M) continue;
-    const int e = e0 + 4 * eg;
-    float* dst = part + (size_t)blockIdx.y * plane + (size_t)t * E + e;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (e + j < E) dst[j] = acc[i][j];
-  }
 }
 
 // One block per token. Wave 0: scores, biased top-k, normalisation; at M > 64 all four waves also
@@ -188,13 +193,14 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
 int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : kLargeParts; }
 
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
+                          uint8_t* x_q, uint8_t* x_s, uint16_t* gate_planes, hipStream_t s) {
   if (M <= kSmallM) {
     router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits,
                                                                                            x_q, x_s);
   } else {
-    router_logits_tiled<<<dim3((M + 63) / 64, kLargeParts, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_w,
-                                                                                            logits);
+    gate_split_kernel<<<dim3(1024), dim3(256), 0, s>>>((size_t)E * H, gate_w, gate_planes);
+    router_logits_mfma<<<dim3((M + 63) / 64, kLargeParts, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_planes,
+                                                                                               logits);
   }
 }
 
