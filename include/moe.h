@@ -164,6 +164,37 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                        uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ---- fp32 partial outputs for a tensor-parallel split of I (section 3 "combine modes"; section 4 "outputs",
+ * modes SLOT and COMBINE). A rank holding I/G of every expert's w1/w3 rows and w2 inputs (dims.inter =
+ * I/G; QDQ blocks never straddle the cut) produces fp32 partial sums; after an all-reduce of the
+ * partials, the exact-official combine rounds each (row, slot) sum to bf16 and adds them in ascending
+ * expert id, as the single-device layer does. */
+
+/* Mode SLOT: as moe_expert_ffn, but slot_f32 [M*k, H] (rows = pair ids t*k + j) receives the unrounded
+ * fp32 sums of h_hat w2[e]^T. h stays in the workspace. */
+moe_status moe_expert_ffn_f32(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                              const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                              const int32_t* offsets, const int32_t* pairs, const int32_t* active, float* slot_f32,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* The shared expert with the unrounded fp32 sums of its w2 (shared_f32 [M, H]) instead of bf16. */
+moe_status moe_shared_expert_f32(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                                 const moe_fp8_expert* shared, float* shared_f32, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Mode COMBINE: out_f32 [M, H] = the token's fp32 slot sums added in fp32 in ascending ids[t, j] order,
+ * then + add[t] (fp32 [M, H], e.g. a shared partial) if add is not NULL. No rounding. */
+moe_status moe_combine_sum_f32(const moe_dims* dims, int32_t M, const int32_t* ids, const float* slot_f32,
+                               const float* add, float* out_f32, void* stream);
+
+/* Exact-official combine of (all-reduced) fp32 slot sums: y = 0 (fp32); y += float(bf16(slot)) over the
+ * token's slots in ascending id order; then y += float(bf16(shared_f32[t])) or float(shared_bf16[t])
+ * (at most one of the two; both NULL = no shared expert); out bf16 [M, H] = bf16(y). With one rank this
+ * equals moe_combine on the bf16 slot outputs bit for bit. */
+moe_status moe_combine_official_f32(const moe_dims* dims, int32_t M, const int32_t* ids, const float* slot_f32,
+                                    const float* shared_f32, const uint16_t* shared_bf16, uint16_t* out,
+                                    void* stream);
+
 /* Bytes of moe_prepare_mxfp4_scales output: 3 * E * I * H / 32 (0 if dims are invalid). */
 size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims);
 

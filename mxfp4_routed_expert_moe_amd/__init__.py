@@ -19,7 +19,8 @@ __all__ = [
     "LIB_PATH", "MoeError", "Dims", "MXFP4Experts", "BF16Experts", "FP8Expert", "lib",
     "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute", "moe_expert_ffn",
     "moe_expert_gemm1", "moe_expert_gemm2", "moe_shared_expert", "moe_combine", "moe_forward", "moe_expand_mxfp4", "workspace",
-    "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales",
+    "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
+    "moe_combine_sum_f32", "moe_combine_official_f32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -81,6 +82,15 @@ lib.moe_combine.restype = _I32
 lib.moe_forward.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
                             ctypes.POINTER(_FP8), _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_forward.restype = _I32
+lib.moe_expert_ffn_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
+                                   _P, _P, _P, _P, _P, _P, _SZ, _P]
+lib.moe_expert_ffn_f32.restype = _I32
+lib.moe_shared_expert_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_FP8), _P, _P, _SZ, _P]
+lib.moe_shared_expert_f32.restype = _I32
+lib.moe_combine_sum_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, _P, _P]
+lib.moe_combine_sum_f32.restype = _I32
+lib.moe_combine_official_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, _P, _P, _P]
+lib.moe_combine_official_f32.restype = _I32
 lib.moe_mxfp4_stage_scales_bytes.argtypes = [ctypes.POINTER(_Dims)]
 lib.moe_mxfp4_stage_scales_bytes.restype = _SZ
 lib.moe_prepare_mxfp4_scales.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
@@ -256,6 +266,42 @@ def moe_combine(dims: Dims, ids, slot_out, shared_out, out, stream=None):
     st = lib.moe_combine(ctypes.byref(dims.c()), M, _ptr(ids, torch.int32), _ptr(slot_out, _BF),
                          _ptr(shared_out, _BF), _ptr(out, _BF), _stream(stream))
     _check(st, "moe_combine")
+
+
+def moe_expert_ffn_f32(dims: Dims, x_q, x_s, packed: MXFP4Experts | None, decoded: BF16Experts | None, rw, offsets,
+                       pairs, active, slot_f32, ws, stream=None):
+    """Mode SLOT: fp32 [M*k, H] unrounded expert outputs (rows = pair ids)."""
+    M = x_q.shape[0]
+    pk = ctypes.byref(packed.c()) if packed is not None else None
+    dc = ctypes.byref(decoded.c()) if decoded is not None else None
+    st = lib.moe_expert_ffn_f32(ctypes.byref(dims.c()), M, _ptr(x_q, torch.uint8), _ptr(x_s, torch.uint8), pk, dc,
+                                _ptr(rw, torch.float32), _ptr(offsets, torch.int32), _ptr(pairs, torch.int32),
+                                _ptr(active, torch.int32), _ptr(slot_f32, torch.float32), _ptr(ws, torch.uint8),
+                                ws.numel(), _stream(stream))
+    _check(st, "moe_expert_ffn_f32")
+
+
+def moe_shared_expert_f32(dims: Dims, x_q, x_s, shared: FP8Expert, shared_f32, ws, stream=None):
+    M = x_q.shape[0]
+    st = lib.moe_shared_expert_f32(ctypes.byref(dims.c()), M, _ptr(x_q, torch.uint8), _ptr(x_s, torch.uint8),
+                                   ctypes.byref(shared.c()), _ptr(shared_f32, torch.float32), _ptr(ws, torch.uint8),
+                                   ws.numel(), _stream(stream))
+    _check(st, "moe_shared_expert_f32")
+
+
+def moe_combine_sum_f32(dims: Dims, ids, slot_f32, add, out_f32, stream=None):
+    M = ids.shape[0]
+    st = lib.moe_combine_sum_f32(ctypes.byref(dims.c()), M, _ptr(ids, torch.int32), _ptr(slot_f32, torch.float32),
+                                 _ptr(add, torch.float32), _ptr(out_f32, torch.float32), _stream(stream))
+    _check(st, "moe_combine_sum_f32")
+
+
+def moe_combine_official_f32(dims: Dims, ids, slot_f32, out, shared_f32=None, shared_bf16=None, stream=None):
+    M = ids.shape[0]
+    st = lib.moe_combine_official_f32(ctypes.byref(dims.c()), M, _ptr(ids, torch.int32),
+                                      _ptr(slot_f32, torch.float32), _ptr(shared_f32, torch.float32),
+                                      _ptr(shared_bf16, _BF), _ptr(out, _BF), _stream(stream))
+    _check(st, "moe_combine_official_f32")
 
 
 def moe_forward(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, decoded: BF16Experts | None,

@@ -178,12 +178,19 @@ __global__ __launch_bounds__(256) void expert_gemm_small(GemmProblem p) {
       } else {
         if (valid) {
           const int orow = p.dense ? pos : p.pairs[pos];
-          uint16_t* o = p.out + (size_t)orow * p.N + n0 + 4 * g;
+          if (p.out_f32) {
+            float* o = p.out_f32 + (size_t)orow * p.N + n0 + 4 * g;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t lo = uint32_t(f32_to_bf16_rne(sum[t][0])) | (uint32_t(f32_to_bf16_rne(sum[t][1])) << 16);
-            const uint32_t hi = uint32_t(f32_to_bf16_rne(sum[t][2])) | (uint32_t(f32_to_bf16_rne(sum[t][3])) << 16);
-            *reinterpret_cast<u32x2*>(o + 16 * t) = u32x2{lo, hi};
+            for (int t = 0; t < 4; ++t)
+              *reinterpret_cast<f32x4*>(o + 16 * t) = f32x4{sum[t][0], sum[t][1], sum[t][2], sum[t][3]};
+          } else {
+            uint16_t* o = p.out + (size_t)orow * p.N + n0 + 4 * g;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t lo = uint32_t(f32_to_bf16_rne(sum[t][0])) | (uint32_t(f32_to_bf16_rne(sum[t][1])) << 16);
+              const uint32_t hi = uint32_t(f32_to_bf16_rne(sum[t][2])) | (uint32_t(f32_to_bf16_rne(sum[t][3])) << 16);
+              *reinterpret_cast<u32x2*>(o + 16 * t) = u32x2{lo, hi};
+            }
           }
         }
       }
@@ -405,13 +412,19 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
       } else {
         if (valid) {
           const int orow = p.dense ? pos : p.pairs[pos];
-          uint16_t* o = p.out + (size_t)orow * p.N + c0 + 4 * g;
           const f32x4 af[4] = {a0, a1, a2, a3};
+          if (p.out_f32) {
+            float* o = p.out_f32 + (size_t)orow * p.N + c0 + 4 * g;
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            const uint32_t lo = uint32_t(f32_to_bf16_rne(af[f][0])) | (uint32_t(f32_to_bf16_rne(af[f][1])) << 16);
-            const uint32_t hi = uint32_t(f32_to_bf16_rne(af[f][2])) | (uint32_t(f32_to_bf16_rne(af[f][3])) << 16);
-            *reinterpret_cast<u32x2*>(o + 16 * f) = u32x2{lo, hi};
+            for (int f = 0; f < 4; ++f) *reinterpret_cast<f32x4*>(o + 16 * f) = af[f];
+          } else {
+            uint16_t* o = p.out + (size_t)orow * p.N + c0 + 4 * g;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+              const uint32_t lo = uint32_t(f32_to_bf16_rne(af[f][0])) | (uint32_t(f32_to_bf16_rne(af[f][1])) << 16);
+              const uint32_t hi = uint32_t(f32_to_bf16_rne(af[f][2])) | (uint32_t(f32_to_bf16_rne(af[f][3])) << 16);
+              *reinterpret_cast<u32x2*>(o + 16 * f) = u32x2{lo, hi};
+            }
           }
         }
       }

@@ -422,12 +422,18 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     } else {
       if (valid && n0 + 128 * wn < p.N) {
         const int orow = p.dense ? pos : p.pairs[pos];
-        uint16_t* o = p.out + (size_t)orow * p.N + n0 + 128 * wn + 4 * g;
+        if (p.out_f32) {
+          float* o = p.out_f32 + (size_t)orow * p.N + n0 + 128 * wn + 4 * g;
 #pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[a][b][0])) | (uint32_t(f32_to_bf16_rne(acc[a][b][1])) << 16);
-          const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[a][b][2])) | (uint32_t(f32_to_bf16_rne(acc[a][b][3])) << 16);
-          *reinterpret_cast<u32x2*>(o + 16 * a) = u32x2{lo, hi};
+          for (int a = 0; a < 8; ++a) *reinterpret_cast<f32x4*>(o + 16 * a) = acc[a][b];
+        } else {
+          uint16_t* o = p.out + (size_t)orow * p.N + n0 + 128 * wn + 4 * g;
+#pragma unroll
+          for (int a = 0; a < 8; ++a) {
+            const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[a][b][0])) | (uint32_t(f32_to_bf16_rne(acc[a][b][1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[a][b][2])) | (uint32_t(f32_to_bf16_rne(acc[a][b][3])) << 16);
+            *reinterpret_cast<u32x2*>(o + 16 * a) = u32x2{lo, hi};
+          }
         }
       }
     }

@@ -61,6 +61,7 @@ struct GemmProblem {
   // outputs
   uint8_t* h_q; uint8_t* h_s;  // GEMM1: QDQ'd h codes [rows, N] and scales [rows, N/32]
   uint16_t* out;               // GEMM2: bf16 [*, N]; row = pair id (routed) or token (dense)
+  float* out_f32;              // GEMM2: if set, the unrounded fp32 sums [*, N] instead of out
   // MXFP4 scales in the stage-major copy made by launch_scales_stage_major (block-scaled MFMA kernels
   // only): [E][K/128][N][4] instead of [E][N][K/32]
   int s_stage_major;
@@ -99,6 +100,13 @@ void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, cons
                        const int32_t* tile_r0, const int32_t* info, hipStream_t s);
 
 // ---- combine (combine.hip) -----------------------------------------------------------------
+// fp32 slot partials (the SLOT mode of the expert FFN). official: y = 0; y += float(bf16(slot)) over the
+// token's slots in ascending id; y += float(bf16(shared_f32)) or float(shared_bf16) if given; out_bf16 =
+// bf16(y). sum: out_f32 = fp32 sum of the slots in ascending id, then + add if given (no rounding).
+void launch_combine_official_f32(int M, int H, int k, const int32_t* ids, const float* slot_f32,
+                                 const float* shared_f32, const uint16_t* shared_bf16, uint16_t* out, hipStream_t s);
+void launch_combine_sum_f32(int M, int H, int k, const int32_t* ids, const float* slot_f32, const float* add,
+                            float* out, hipStream_t s);
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,
                     const uint16_t* shared_out, uint16_t* out, hipStream_t s);
 

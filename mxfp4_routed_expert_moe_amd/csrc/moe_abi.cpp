@@ -211,7 +211,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
 // GEMM2: H rows of w2 over I inputs; activation row = sorted position; output row = pair id.
 void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, const moe_mxfp4_experts* packed,
               const moe_bf16_experts* decoded, const int32_t* offsets, const int32_t* pairs, const int32_t* active,
-              uint16_t* slot, const TileMap& tm, hipStream_t s) {
+              uint16_t* slot, float* slot_f32, const TileMap& tm, hipStream_t s) {
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem q{};
@@ -229,7 +229,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   }
   q.N = H; q.K = I;
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
-  q.out = slot;
+  q.out = slot; q.out_f32 = slot_f32;
   if (routed_mfma(d, M, packed)) {
     if (packed->stage_scales != nullptr) {
       q.sa = packed->stage_scales + stage_scales_off(d, 2);
@@ -250,19 +250,19 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
 // their own stage-major layout.
 void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
                    const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
-                   const int32_t* active, uint16_t* slot, uint8_t* hq, uint8_t* hs, bool h_internal, void* ws,
-                   hipStream_t s) {
+                   const int32_t* active, uint16_t* slot, float* slot_f32, uint8_t* hq, uint8_t* hs, bool h_internal,
+                   void* ws, hipStream_t s) {
   TileMap tm;
   if (routed_mfma(d, M, packed)) {
     tm = make_tile_map(d, M, offsets, ws, s);
     tm.act_sm = h_internal;
   }
   do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, tm, s);
-  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, tm, s);
+  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, slot_f32, tm, s);
 }
 
 void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_fp8_expert* sh,
-               uint8_t* shq, uint8_t* shs, uint16_t* out, hipStream_t s) {
+               uint8_t* shq, uint8_t* shs, uint16_t* out, float* out_f32, hipStream_t s) {
   const int H = d->hidden, I = d->inter;
   GemmProblem p{};
   p.dense = 1; p.M = M; p.k = 1; p.num_experts = 1;
@@ -278,7 +278,7 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
   q.wa = sh->w2; q.sa = sh->s2; q.wb = nullptr; q.sb = nullptr;
   q.N = H; q.K = I;
   q.act_q = shq; q.act_s = shs; q.act_by_token = 0;
-  q.out = out;
+  q.out = out; q.out_f32 = out_f32;
   if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, none.info, s);
   else moe::launch_gemm2_stream(moe::W_FP8_BLOCK32, q, 1, s);
 }
@@ -344,8 +344,8 @@ moe_status moe_expert_ffn(const moe_dims* dims, int32_t M, const uint8_t* x_q, c
     h_q = at<uint8_t>(ws, L.h_q);
     h_s = at<uint8_t>(ws, L.h_s);
   }
-  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, h_q, h_s, h_internal, ws,
-                static_cast<hipStream_t>(stream));
+  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, slot_out, nullptr, h_q, h_s,
+                h_internal, ws, static_cast<hipStream_t>(stream));
   return launched();
 }
 
@@ -382,7 +382,7 @@ moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   TileMap tm;
   if (routed_mfma(dims, M, packed)) tm = make_tile_map(dims, M, offsets, ws, s);
-  do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, tm, s);
+  do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, nullptr, tm, s);
   return launched();
 }
 
@@ -395,7 +395,7 @@ moe_status moe_shared_expert(const moe_dims* dims, int32_t M, const uint8_t* x_q
   if (!al(x_q, 16) || !al(x_s, 16) || !al(shared_out, 16)) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   const WsLayout L = ws_layout(dims, M);
-  do_shared(dims, M, x_q, x_s, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), shared_out,
+  do_shared(dims, M, x_q, x_s, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), shared_out, nullptr,
             static_cast<hipStream_t>(stream));
   return launched();
 }
@@ -445,14 +445,71 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                         at<int32_t>(ws, L.inv), active, s);
   }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
-  do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, at<uint8_t>(ws, L.h_q),
+  do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
                 at<uint8_t>(ws, L.h_s), true, ws, s);
   uint16_t* sh_out = nullptr;
   if (shared != nullptr) {
     sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
-    do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, s);
+    do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
   }
   moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+  return launched();
+}
+
+moe_status moe_expert_ffn_f32(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                              const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const float* rw,
+                              const int32_t* offsets, const int32_t* pairs, const int32_t* active, float* slot_f32,
+                              void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (!al(x_q, 16) || !al(x_s, 16) || !al(rw, 4) || !al(offsets, 4) || !al(pairs, 4) || !al(active, 4) ||
+      !al(slot_f32, 16))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  const WsLayout L = ws_layout(dims, M);
+  do_expert_ffn(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, nullptr, slot_f32,
+                at<uint8_t>(ws, L.h_q), at<uint8_t>(ws, L.h_s), true, ws, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_shared_expert_f32(const moe_dims* dims, int32_t M, const uint8_t* x_q, const uint8_t* x_s,
+                                 const moe_fp8_expert* shared, float* shared_f32, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  MOE_TRY(check_shared(shared));
+  if (!al(x_q, 16) || !al(x_s, 16) || !al(shared_f32, 16)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(dims, M, ws, ws_bytes));
+  const WsLayout L = ws_layout(dims, M);
+  do_shared(dims, M, x_q, x_s, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), nullptr, shared_f32,
+            static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_combine_sum_f32(const moe_dims* dims, int32_t M, const int32_t* ids, const float* slot_f32,
+                               const float* add, float* out_f32, void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  if (!al(ids, 4) || !al(slot_f32, 16) || !al(out_f32, 16)) return MOE_ERR_INVALID_ARG;
+  if (add != nullptr && !al(add, 16)) return MOE_ERR_INVALID_ARG;
+  moe::launch_combine_sum_f32(M, dims->hidden, dims->top_k, ids, slot_f32, add, out_f32,
+                              static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_combine_official_f32(const moe_dims* dims, int32_t M, const int32_t* ids, const float* slot_f32,
+                                    const float* shared_f32, const uint16_t* shared_bf16, uint16_t* out,
+                                    void* stream) {
+  MOE_TRY(check_dims(dims, M));
+  if (M == 0) return MOE_OK;
+  if (!al(ids, 4) || !al(slot_f32, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (shared_f32 != nullptr && shared_bf16 != nullptr) return MOE_ERR_INVALID_ARG;
+  if ((shared_f32 != nullptr && !al(shared_f32, 16)) || (shared_bf16 != nullptr && !al(shared_bf16, 16)))
+    return MOE_ERR_INVALID_ARG;
+  moe::launch_combine_official_f32(M, dims->hidden, dims->top_k, ids, slot_f32, shared_f32, shared_bf16, out,
+                                   static_cast<hipStream_t>(stream));
   return launched();
 }
 

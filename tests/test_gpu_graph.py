@@ -77,3 +77,55 @@ def test_graph_replay_equals_eager_on_changed_inputs(cid, over, with_shared):
         assert torch.equal(g_buf["ids"], e_buf["ids"]), f"replay {it}: routing differs from eager"
         assert torch.equal(g_buf["rw"], e_buf["rw"]), f"replay {it}: route weights differ from eager"
         assert torch.equal(g_buf["out"], e_buf["out"]), f"replay {it}: output differs from eager"
+
+
+def test_graph_replay_of_the_fp32_slot_and_combine_modes():
+    """route -> permute -> SLOT fp32 expert FFN -> COMBINE fp32 sum and exact-official combine, captured
+    once and replayed on changed activations: every replay equals the eager calls bit for bit."""
+    cfg, inp = inputs(0, M=300, H=256, I=128, E=8, k=2)
+    d = upload(inp)
+    M, k, H, E = cfg.M, cfg.k, cfg.H, cfg.E
+    dims = dims_of(cfg)
+    dev = dict(device="cuda")
+
+    def bufs():
+        return dict(ws=m().workspace(dims, M), x=d["x"].clone(),
+                    ids=torch.empty((M, k), dtype=torch.int32, **dev), rw=torch.empty((M, k), dtype=torch.float32, **dev),
+                    xq=torch.empty((M, H), dtype=torch.uint8, **dev), xs=torch.empty((M, H // 32), dtype=torch.uint8, **dev),
+                    counts=torch.empty(E, dtype=torch.int32, **dev), offsets=torch.empty(E + 1, dtype=torch.int32, **dev),
+                    pairs=torch.empty(M * k, dtype=torch.int32, **dev), active=torch.empty(E, dtype=torch.int32, **dev),
+                    slot=torch.empty((M * k, H), dtype=torch.float32, **dev),
+                    sum=torch.empty((M, H), dtype=torch.float32, **dev), out=torch.empty((M, H), dtype=torch.int16, **dev))
+
+    def run(b):
+        m().moe_route(dims, b["x"], d["gate_w"], d["gate_b"], b["ids"], b["rw"], b["xq"], b["xs"], b["ws"])
+        m().moe_permute(dims, b["ids"], b["counts"], b["offsets"], b["pairs"], None, b["active"])
+        m().moe_expert_ffn_f32(dims, b["xq"], b["xs"], packed_of(d), None, b["rw"], b["offsets"], b["pairs"],
+                               b["active"], b["slot"], b["ws"])
+        m().moe_combine_sum_f32(dims, b["ids"], b["slot"], None, b["sum"])
+        m().moe_combine_official_f32(dims, b["ids"], b["slot"], b["out"])
+
+    g_buf, e_buf = bufs(), bufs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(g_buf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g_buf)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for it in range(4):
+        xb = inp["x"][rng.permutation(M)].copy()
+        xt = dev_tensor(xb)
+        g_buf["x"].copy_(xt)
+        e_buf["x"].copy_(xt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        run(e_buf)
+        torch.cuda.synchronize()
+        for key in ("ids", "slot", "sum", "out"):
+            assert torch.equal(g_buf[key], e_buf[key]), f"replay {it}: {key} differs from eager"
