@@ -107,41 +107,72 @@ __global__ __launch_bounds__(256) void gate_split_kernel(size_t n, const float* 
   }
 }
 
-// Block: 64 tokens x 128 experts over one quarter of H (the quarters are added in ascending order by the
-// select kernel). Wave w takes experts 32 w .. 32 w + 31 (two 16-wide B tiles) for all 64 tokens (four A
-// tiles). Per 32-wide K step, in ascending order: for each tile the hi, mid and lo products
-// (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column l % 16 of B, inputs
-// 8 (l / 16) .. + 7 of the step; the result (4 (l / 16) + v, l % 16) is accumulator v of lane l).
-__global__ __launch_bounds__(256) void router_logits_mfma(int M, int H, int E, const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ gp, float* __restrict__ part) {
+// Block: 128 tokens x 128 experts over one quarter of H (the quarters are added in ascending order by the
+// select kernel). Per 32-wide K step, the block's x tile (128 rows x 64 B) and the three gate-plane tiles
+// (128 rows x 64 B each) stream into a three-stage LDS ring through direct global -> LDS copies, issued
+// two steps ahead; one copy per wave per tile (16 rows). The 16-byte chunks of each 64-byte LDS row are
+// XOR-swizzled (chunk ^ ((r ^ r >> 2) & 3)) so that the 16 rows of a fragment read distinct banks.
+// Wave w computes tokens 64 (w / 4) .. + 63 (four A tiles) x experts 32 (w % 4) .. + 31 (two B tiles):
+// per step and tile the hi, mid and lo products, in that order (v_mfma_f32_16x16x32_bf16: lane l
+// supplies row l % 16 of A and column l % 16 of B, inputs 8 (l / 16) .. + 7 of the step; the result
+// (4 (l / 16) + v, l % 16) is accumulator v of lane l).
+constexpr int kRtStages = 3;
+struct RouterStage {
+  uint16_t x[128 * 32];
+  uint16_t g[3][128 * 32];
+};
+
+__device__ __forceinline__ int rt_key(int r) { return (r ^ (r >> 2)) & 3; }
+
+__global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E, const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ gp, float* __restrict__ part) {
+  __shared__ __align__(16) RouterStage ring[kRtStages];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.z * 128 + 32 * wave;
-  const int hq = H / kLargeParts, hbeg = blockIdx.y * hq;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.z * 128;
+  const int hq = H / kLargeParts, hbeg = blockIdx.y * hq, nk = hq / 32;
   const size_t plane = (size_t)E * H;
-  const uint16_t* xr[4];
+  // copy sources: lane i of wave w fills LDS row 16 w + i / 4, physical chunk i % 4 (logical chunk
+  // (i % 4) ^ key); rows past M or E repeat the last row
+  const int dr = 16 * wave + (lane >> 2), lc = (lane & 3) ^ rt_key(dr);
+  const uint16_t* xsrc = x + (size_t)min(t0 + dr, M - 1) * H + hbeg + 8 * lc;
+  const uint16_t* gsrc = gp + (size_t)min(e0 + dr, E - 1) * H + hbeg + 8 * lc;
+  auto copy16 = [](const uint16_t* src, uint16_t* lds) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (__attribute__((address_space(3))) void*)lds, 16,
+                                     0, 0);
+  };
+  auto issue = [&](int s) {
+    RouterStage& st = ring[s % kRtStages];
+    const int h = s * 32;
+    copy16(xsrc + h, &st.x[16 * wave * 32]);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) xr[a] = x + (size_t)min(t0 + 16 * a + r16, M - 1) * H + hbeg + 8 * g;
-  const uint16_t* gr[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) gr[b] = gp + (size_t)min(e0 + 16 * b + r16, E - 1) * H + hbeg + 8 * g;
+    for (int q = 0; q < 3; ++q) copy16(gsrc + q * plane + h, &st.g[q][16 * wave * 32]);
+  };
+  const int th = wave >> 2, eq = wave & 3;
   f32x4 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int h, u32x4 (&A)[4], u32x4 (&B)[2][3]) {
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int s = 0; s < nk; ++s) {
+    // this wave's copies of step s have landed (those of step s + 1 may still be in flight), then meet
+    if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 2 < nk) issue(s + 2);   // into the slot read at step s - 1: every wave is past it
+    const RouterStage& st = ring[s % kRtStages];
+    u32x4 A[4], B[2][3];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) A[a] = *reinterpret_cast<const u32x4*>(xr[a] + h);
+    for (int a = 0; a < 4; ++a) {
+      const int r = 64 * th + 16 * a + r16;
+      A[a] = *reinterpret_cast<const u32x4*>(&st.x[r * 32 + 8 * (g ^ rt_key(r))]);
+    }
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      const int r = 32 * eq + 16 * b + r16;
 #pragma unroll
-      for (int q = 0; q < 3; ++q) B[b][q] = *reinterpret_cast<const u32x4*>(gr[b] + q * plane + h);
-  };
-  u32x4 A[4], B[2][3];
-  load(0, A, B);
-  for (int h = 0; h < hq; h += 32) {
-    u32x4 An[4], Bn[2][3];
-    if (h + 32 < hq) load(h + 32, An, Bn);
+      for (int q = 0; q < 3; ++q) B[b][q] = *reinterpret_cast<const u32x4*>(&st.g[q][r * 32 + 8 * (g ^ rt_key(r))]);
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -150,24 +181,16 @@ __global__ __launch_bounds__(256) void router_logits_mfma(int M, int H, int E, c
         for (int q = 0; q < 3; ++q)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[a]),
                                                              __builtin_bit_cast(bf16x8, B[b][q]), acc[a][b], 0, 0, 0);
-    if (h + 32 < hq) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) A[a] = An[a];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int q = 0; q < 3; ++q) B[b][q] = Bn[b][q];
-    }
   }
   float* out = part + (size_t)blockIdx.y * M * E;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int e = e0 + 16 * b + r16;
+      const int e = e0 + 32 * eq + 16 * b + r16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int t = t0 + 16 * a + 4 * g + v;
+        const int t = t0 + 64 * th + 16 * a + 4 * g + v;
         if (t < M && e < E) out[(size_t)t * E + e] = acc[a][b][v];
       }
     }
@@ -199,8 +222,8 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
                                                                                            x_q, x_s);
   } else {
     gate_split_kernel<<<dim3(1024), dim3(256), 0, s>>>((size_t)E * H, gate_w, gate_planes);
-    router_logits_mfma<<<dim3((M + 63) / 64, kLargeParts, (E + 127) / 128), dim3(256), 0, s>>>(M, H, E, x, gate_planes,
-                                                                                               logits);
+    router_logits_mfma<<<dim3((M + 127) / 128, kLargeParts, (E + 127) / 128), dim3(512), 0, s>>>(M, H, E, x, gate_planes,
+                                                                                                logits);
   }
 }
 
