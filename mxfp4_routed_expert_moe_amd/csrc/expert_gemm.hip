@@ -168,9 +168,7 @@ __global__ __launch_bounds__(256) void expert_gemm_small(GemmProblem p) {
         if (valid) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
+            const uint32_t packed = qdq_code4(h[half][0], h[half][1], h[half][2], h[half][3], inv);
             *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + n0 + 16 * half + 4 * g) = packed;
           }
           if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + n0 / 32] = uint8_t(E8 + 127);
@@ -402,9 +400,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
         if (valid) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
+            const uint32_t packed = qdq_code4(h[half][0], h[half][1], h[half][2], h[half][3], inv);
             *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + c0 + 16 * half + 4 * g) = packed;
           }
           if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + c0 / 32] = uint8_t(E8 + 127);

@@ -406,9 +406,7 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
           const int col0 = n0 + 64 * wn + 32 * qb;
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            uint32_t packed = 0;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) packed |= qdq_code(h[half][v], inv) << (8 * v);
+            const uint32_t packed = qdq_code4(h[half][0], h[half][1], h[half][2], h[half][3], inv);
             *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + col0 + 16 * half + 4 * g) = packed;
           }
           if (g == 0) {

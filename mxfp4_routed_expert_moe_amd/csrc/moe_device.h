@@ -74,6 +74,15 @@ __device__ __forceinline__ uint32_t qdq_code(float x, float inv_scale) {
   return e4m3_encode_rne(q);
 }
 
+// Four QDQ codes packed little-endian into a dword (x0 in the low byte), with the gfx950 FP8 converter
+// (v_cvt_pk_fp8_f32: E4M3fn, round to nearest even, subnormals kept) on the clamped quotients; equal
+// to qdq_code on every bf16 input (checked exhaustively on the GPU).
+__device__ __forceinline__ uint32_t qdq_code4(float x0, float x1, float x2, float x3, float inv_scale) {
+  auto q = [&](float x) { return fminf(fmaxf(x * inv_scale, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q(x0), q(x1), 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(q(x2), q(x3), lo, true));
+}
+
 // Packed FP4 byte -> two bf16 (low nibble first) times the E8M0 scale, via the gfx950 converter
 template <int BYTE>
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t packed4, float scale) {

@@ -18,30 +18,48 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
                                                        int32_t* __restrict__ active) {
   __shared__ int hist[256];
-  __shared__ int wave_cnt[kPermWaves];
+  __shared__ int wave_cnt[kPermWaves], wave_below[kPermWaves];
   __shared__ int base_off;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+  if (e == 0)
+    for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
   __syncthreads();
-  // each wave owns a contiguous segment of the pair list (a multiple of 64 long)
+  // each wave owns a contiguous segment of the pair list (a multiple of 64 long). Block e counts the
+  // pairs of expert e and those of lower experts with wave ballots; only block 0 builds the full
+  // histogram (for the active list and the total).
   const int seg = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;
   const int beg = wave * seg, end = min(P, beg + seg);
-  int mine = 0;
-  for (int i = beg + lane; i < beg + seg; i += 64) {
-    int v = -1;
-    if (i < end) v = ids[i];
-    const bool ok = v >= 0 && v < E;
-    if (ok) atomicAdd(&hist[v], 1);
-    mine += __popcll(__ballot(ok && v == e));
+  int mine = 0, lower = 0;
+  constexpr int U = 8;   // ids in flight per lane
+  for (int i0 = beg; i0 < end; i0 += 64 * U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u + lane;
+      v[u] = i < end ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = v[u] >= 0 && v[u] < E;
+      if (e == 0 && ok) atomicAdd(&hist[v[u]], 1);
+      mine += __popcll(__ballot(ok && v[u] == e));
+      lower += __popcll(__ballot(ok && v[u] < e));
+    }
   }
-  if (lane == 0) wave_cnt[wave] = mine;
+  if (lane == 0) {
+    wave_cnt[wave] = mine;
+    wave_below[wave] = lower;
+  }
   __syncthreads();
   if (tid == 0) {
-    int off = 0;
-    for (int j = 0; j < e; ++j) off += hist[j];
+    int off = 0, cnt = 0;
+    for (int w = 0; w < kPermWaves; ++w) {
+      off += wave_below[w];
+      cnt += wave_cnt[w];
+    }
     base_off = off;
-    counts[e] = hist[e];
+    counts[e] = cnt;
     offsets[e] = off;
     if (e == 0) {
       int tot = 0, na = 0;
@@ -57,17 +75,25 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
   int base = base_off;
   for (int w = 0; w < wave; ++w) base += wave_cnt[w];
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i = beg + lane; i < beg + seg; i += 64) {
-    int v = -1;
-    if (i < end) v = ids[i];
-    const bool hit = (v == e);
-    const unsigned long long m = __ballot(hit);
-    if (hit) {
-      const int pos = base + __popcll(m & below);
-      pairs[pos] = i;
-      if (inv) inv[i] = pos;
+  for (int i0 = beg; i0 < end; i0 += 64 * U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u + lane;
+      v[u] = i < end ? ids[i] : -1;
     }
-    base += __popcll(m);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 64 * u + lane;
+      const bool hit = (v[u] == e);
+      const unsigned long long m = __ballot(hit);
+      if (hit) {
+        const int pos = base + __popcll(m & below);
+        pairs[pos] = i;
+        if (inv) inv[i] = pos;
+      }
+      base += __popcll(m);
+    }
   }
 }
 

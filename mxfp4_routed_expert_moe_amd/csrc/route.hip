@@ -196,20 +196,20 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
     }
 }
 
-// One block per token. Wave 0: scores, biased top-k, normalisation; at M > 64 all four waves also
-// QDQ the token's row (one 32-wide block per thread); at M <= 64 the logits kernel has done it.
+// One wave per token, four tokens per block: scores, biased top-k, normalisation; at M > 64 the wave
+// also QDQs the token's row (one 32-wide block per lane per pass); at M <= 64 the logits kernel has.
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
                                                          int nparts, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
                                                          const uint16_t* __restrict__ x,
                                                          int32_t* __restrict__ ids, float* __restrict__ rw,
                                                          uint8_t* __restrict__ x_q, uint8_t* __restrict__ x_s) {
-  const int t = blockIdx.x;
-  if (threadIdx.x < 64)
-    select_token(t, M, E, k, route_scale, nparts, logits, gate_b, threadIdx.x, ids, rw, nullptr, nullptr);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= M) return;
+  select_token(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, nullptr, nullptr);
   if (M <= kSmallM) return;
   const int nb = H / 32;
-  for (int b = threadIdx.x; b < nb; b += 256)
+  for (int b = lane; b < nb; b += 64)
     qdq_block32(x + (size_t)t * H + b * 32, x_q + (size_t)t * H + b * 32, x_s + (size_t)t * nb + b);
 }
 
@@ -230,7 +230,7 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
                               uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  router_select_qdq<<<dim3(M), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
+  router_select_qdq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
                                                             logits, gate_b, x, ids, rw, x_q, x_s);
 }
 

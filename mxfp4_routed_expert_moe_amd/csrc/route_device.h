@@ -158,9 +158,7 @@ __device__ __forceinline__ void qdq_block32(const uint16_t* __restrict__ src, ui
   u32x4 out[2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t c0 = qdq_code(v[4 * i], inv), c1 = qdq_code(v[4 * i + 1], inv);
-    const uint32_t c2 = qdq_code(v[4 * i + 2], inv), c3 = qdq_code(v[4 * i + 3], inv);
-    out[i >> 2][i & 3] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    out[i >> 2][i & 3] = qdq_code4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], inv);
   }
   u32x4* dst = reinterpret_cast<u32x4*>(q);
   dst[0] = out[0];
