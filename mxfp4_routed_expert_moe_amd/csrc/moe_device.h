@@ -25,12 +25,8 @@ __device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_
 // bf16 bit pattern -> fp32 (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bits_to_f32(uint32_t(b) << 16); }
 
-// fp32 -> bf16 bit pattern, round to nearest even (inputs are finite)
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = f32_to_bits(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// fp32 -> bf16 bit pattern, round to nearest even (inputs are finite): one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // fp32 -> the bf16 value it rounds to, as an fp32
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16_rne(f)); }
@@ -97,15 +93,37 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed8, float scal
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// e^x in fp32 as 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32, 1 ulp). The product
+// x log2 e is carried as hi + lo: hi = fp32(x * L2E_HI), lo = the exact error of that product (an FMA)
+// plus x * L2E_LO, where L2E_HI + L2E_LO is log2 e to twice fp32 precision (a Cody-Waite split); then
+// e^x = 2^hi (1 + lo ln 2). Overflow (x above ln FLT_MAX) returns +inf.
+__device__ __forceinline__ float exp_f32(float x) {
+  constexpr float kL2eHi = 1.44269502162933349609375f;   // fp32(log2 e)
+  constexpr float kL2eLo = 1.9259629911266175e-8f;       // log2 e - kL2eHi
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float hi = x * kL2eHi;
+  const float lo = fmaf(x, kL2eLo, fmaf(x, kL2eHi, -hi));
+  const float p = __builtin_amdgcn_exp2f(hi);
+  return x > 88.72f ? __builtin_inff() : fmaf(p, lo * kLn2, p);
+}
+
+// g / d for d >= 1 or d = +inf: hardware reciprocal (1 ulp), then one FMA correction of the quotient
+// from its exact residual g - d q.
+__device__ __forceinline__ float div_by_ge1(float g, float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = g * r;
+  const float q2 = fmaf(fmaf(-d, q, g), r, q);
+  return d == __builtin_inff() ? g * 0.0f : q2;
+}
+
 // SwiGLU of the routed/shared expert (section 2 "Expert", section 4 math): g and u are the
 // bf16-rounded linear outputs; u is clamped to [-10, 10] and g to at most 10; then
 // h = (g / (1 + exp(-g))) * u in fp32, times the route weight rw (1 for the shared expert).
 __device__ __forceinline__ float swiglu(float g, float u, float rw, bool weighted) {
   g = fminf(g, 10.0f);
   u = fminf(fmaxf(u, -10.0f), 10.0f);
-  float e = expf(-g);                            // full-precision exp (ROCm device library)
-  float d = 1.0f + e;
-  float h = (g / d) * u;
+  const float d = 1.0f + exp_f32(-g);
+  float h = div_by_ge1(g, d) * u;
   if (weighted) h = rw * h;
   return h;
 }
