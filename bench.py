@@ -209,6 +209,55 @@ def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
     return res
 
 
+def measure_dense(M: int = 8, reps: int = 40, replicas: int = 4) -> dict:
+    """The dense FP8 projection family at decode width: moe_fp8_linear per shape, with the weights in R
+    replicas (rotated, so the last-level cache cannot serve them). The calls are captured once in a HIP
+    graph (the library is graph-safe) and the replays timed with HIP events, so host launch overhead
+    does not enter the per-call time."""
+    import numpy as np
+    import torch
+
+    import mxfp4_routed_expert_moe_amd as moe
+    import synth
+
+    out = {}
+    for name, (N, K) in synth.DENSE_SHAPES.items():
+        inp = synth.make_dense_inputs(N, K, M)
+        x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+        ws_ = [(torch.from_numpy(inp["w"]).cuda(), torch.from_numpy(inp["s"]).cuda()) for _ in range(replicas)]
+        y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        work = moe.fp8_linear_workspace(M, N, K)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(2 * replicas):
+                moe.moe_fp8_linear(x, *ws_[i % replicas], y=y, ws=work)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        per_graph = 2 * replicas
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(per_graph):
+                moe.moe_fp8_linear(x, *ws_[i % replicas], y=y, ws=work)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_rep = max(1, reps // per_graph)
+        e0.record()
+        for _ in range(n_rep):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (n_rep * per_graph)
+        del graph
+        nbytes = N * K + (N // 32) * (K // 32) + M * K * 2 + M * N * 2
+        out[name] = dict(N=N, K=K, us=round(us, 2), gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                         hbm_frac=round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4))
+        del ws_, work
+    torch.cuda.empty_cache()
+    return dict(workload=f"dense FP8 projections at M={M}", bound="hbm", unit="GB/s", shapes=out)
+
+
 def calibrate_copy(gib: int = 1, reps: int = 5) -> dict:
     """A plain device-to-device copy of a known size (the reference for the L2 byte counters)."""
     import torch
@@ -254,6 +303,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the rocprof byte counters)")
     args = ap.parse_args()
@@ -283,6 +333,11 @@ def main():
                        ms_per_step=round(p["ms_per_step"], 4), kernel_us={k: round(v, 1) for k, v in
                                                                           p["kernel_us"].items()},
                        layer_tflops=round(p["layer_tflops"], 1), roofline=p["roofline"])
+    dense = None
+    if not args.no_dense:
+        dense = measure_dense()
+        summary = ", ".join(f"{k}: {v['us']} us" for k, v in dense["shapes"].items())
+        print(f"# dense: {summary}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
@@ -307,6 +362,7 @@ def main():
         "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
         "roofline": r["roofline"],
         "prefill": prefill,
+        "dense_fp8": dense,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -195,6 +195,17 @@ moe_status moe_combine_official_f32(const moe_dims* dims, int32_t M, const int32
                                     const float* shared_f32, const uint16_t* shared_bf16, uint16_t* out,
                                     void* stream);
 
+/* ---- Dense FP8 linear (section 4 "Dense", the projection family wq_a 1280 x 5120, wkv 512 x 5120,
+ * wq_b 16384 x 1280, wo_b 5120 x 4096, main_proj 5120 x 15360, shared w1/w3/w2): y = bf16(act_qdq(x) W^T)
+ * with W FP8 E4M3 uint8 [N, K] and one E8M0 scale per 32x32 block, s uint8 [N/32, K/32]; act_qdq is the
+ * per-32 E4M3 QDQ of each row of x (section 2 "Quantized linear"). x bf16 [M, K]; exactly one of y
+ * (bf16 [M, N]) or y_f32 (the unrounded fp32 sums [M, N], e.g. a tensor-parallel partial) is given.
+ * N and K multiples of 128 (at most 65536), M*K and M*N at most 2^31. The workspace holds the QDQ'd x
+ * and, at M <= 64, the partial sums of the split inner dimension. */
+size_t moe_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, const uint8_t* s,
+                          uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of moe_prepare_mxfp4_scales output: 3 * E * I * H / 32 (0 if dims are invalid). */
 size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims);
 

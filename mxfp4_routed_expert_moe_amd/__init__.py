@@ -20,7 +20,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_status_str", "moe_route", "moe_permute", "moe_expert_ffn",
     "moe_expert_gemm1", "moe_expert_gemm2", "moe_shared_expert", "moe_combine", "moe_forward", "moe_expand_mxfp4", "workspace",
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
-    "moe_combine_sum_f32", "moe_combine_official_f32",
+    "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -91,6 +91,10 @@ lib.moe_combine_sum_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, _P,
 lib.moe_combine_sum_f32.restype = _I32
 lib.moe_combine_official_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, _P, _P, _P]
 lib.moe_combine_official_f32.restype = _I32
+lib.moe_fp8_linear_workspace_bytes.argtypes = [_I32, _I32, _I32]
+lib.moe_fp8_linear_workspace_bytes.restype = _SZ
+lib.moe_fp8_linear.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+lib.moe_fp8_linear.restype = _I32
 lib.moe_mxfp4_stage_scales_bytes.argtypes = [ctypes.POINTER(_Dims)]
 lib.moe_mxfp4_stage_scales_bytes.restype = _SZ
 lib.moe_prepare_mxfp4_scales.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
@@ -341,3 +345,29 @@ def moe_prepare_mxfp4_scales(dims: Dims, packed: MXFP4Experts, out=None, stream=
                                       _stream(stream))
     _check(st, "moe_prepare_mxfp4_scales")
     return out
+
+
+def moe_fp8_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib.moe_fp8_linear_workspace_bytes(M, N, K))
+
+
+def fp8_linear_workspace(M: int, N: int, K: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor for moe_fp8_linear (256-byte aligned)."""
+    n = moe_fp8_linear_workspace_bytes(M, N, K)
+    if n == 0:
+        raise MoeError("unsupported dense linear shape")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def moe_fp8_linear(x, w, s, y=None, y_f32=None, ws=None, stream=None):
+    """y = bf16(act_qdq(x) W^T): x bf16 [M, K], w uint8 E4M3 [N, K], s uint8 E8M0 [N/32, K/32]; exactly
+    one of y (bf16 [M, N]) or y_f32 (fp32 [M, N])."""
+    M, K = x.shape
+    N = w.shape[0]
+    if ws is None:
+        ws = fp8_linear_workspace(M, N, K, device=x.device)
+    st = lib.moe_fp8_linear(M, N, K, _ptr(x, _BF), _ptr(w, torch.uint8), _ptr(s, torch.uint8), _ptr(y, _BF),
+                            _ptr(y_f32, torch.float32), _ptr(ws, torch.uint8), ws.numel(), _stream(stream))
+    _check(st, "moe_fp8_linear")

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "combine.hip", "expand.hip",
-           "moe_abi.cpp"]
+           "dense.hip", "moe_abi.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,199 @@
+// Dense FP8 linear of the method's projection family (DeepSeek-V4.1-Flash native-tensor page, section 4
+// "Dense"): y = bf16(sum_k act_qdq(x) W) with W FP8 E4M3 [N, K] and one E8M0 scale per 32x32 block,
+// the same numerics as the shared expert's w2 (section 2 "Quantized linear").
+//
+// Decode widths (M <= 64): the weights stream from HBM once through the block-scaled matrix cores, with
+// the inner dimension split across blocks so that even N = 512 fills the chip. Block (c, z) owns 64
+// weight rows (one 16-row fragment per wave) and the z-th run of 128-wide K steps; the M activation
+// rows of that run (E4M3 codes and scales) and the two 32-row weight-scale rows are copied into LDS
+// once. The partial sums of the runs are added in ascending run order by a second kernel (fp32, then
+// bf16 or fp32 out). Wider batches use the prefill-width grouped GEMM as a single expert.
+//
+// Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E4M3 operand holds K
+// [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of the step; lane l supplies the E8M0 scale of K block g
+// of its row; the result (4g + v, l % 16) is accumulator v of lane l.
+#include <algorithm>
+
+#include "kernels.h"
+#include "moe_device.h"
+#include "route_device.h"
+
+namespace moe {
+
+// Per-32 E4M3 QDQ of every row of x [M, K] (K a multiple of 32): thread per 32-wide block.
+__global__ __launch_bounds__(256) void qdq_rows_kernel(long long nblk, const uint16_t* __restrict__ x,
+                                                       uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  for (long long b = (long long)blockIdx.x * 256 + threadIdx.x; b < nblk; b += (long long)gridDim.x * 256)
+    qdq_block32(x + b * 32, xq + b * 32, xs + b);
+}
+
+void launch_qdq_rows(int M, int K, const uint16_t* x, uint8_t* xq, uint8_t* xs, hipStream_t s) {
+  const long long nblk = (long long)M * (K / 32);
+  const int grid = (int)std::min<long long>((nblk + 255) / 256, 4096);
+  qdq_rows_kernel<<<dim3(grid), dim3(256), 0, s>>>(nblk, x, xq, xs);
+}
+
+namespace {
+
+// copy of a run of nbytes (a multiple of UNIT) straight into LDS by one wave
+template <int UNIT>
+__device__ __forceinline__ void dense_run(uint8_t* lds, const uint8_t* src, int nbytes, int lane) {
+  for (int off = 0; off < nbytes; off += 64 * UNIT)
+    if (off + UNIT * lane < nbytes) {
+      const void* g = static_cast<const void*>(src + off + UNIT * lane);
+      auto* l = (__attribute__((address_space(3))) void*)(lds + off);
+      if constexpr (UNIT == 16) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+    }
+}
+
+}  // namespace
+
+// Dynamic LDS: activation codes [M][S * 128], activation scales [M][S * 4], weight scales [2][S * 4]
+// (S = steps of this run).
+__global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, int steps_per_run,
+                                                         const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                                         const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
+                                                         float* __restrict__ part, uint16_t* __restrict__ y,
+                                                         float* __restrict__ y32) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const int nk = K / 128, KB = K / 32;
+  const int lo = blockIdx.y * steps_per_run, hi = min(nk, lo + steps_per_run), ns = hi - lo;
+  if (ns <= 0) return;
+  const int n0 = blockIdx.x * 64;
+  uint8_t* xb = dyn;                                   // [M][steps_per_run * 128]
+  uint8_t* xsb = xb + M * steps_per_run * 128;         // [M][steps_per_run * 4]
+  uint8_t* wsb = xsb + M * steps_per_run * 4;          // [2][steps_per_run * 4]
+  const int RL = steps_per_run * 128, SL = steps_per_run * 4;
+  {
+    int run = 0;
+    auto mine = [&]() { return (run++ & 3) == wave; };
+    for (int t = 0; t < M; ++t) {
+      if (mine()) dense_run<16>(xb + t * RL, xq + (size_t)t * K + lo * 128, ns * 128, lane);
+      if (mine()) dense_run<4>(xsb + t * SL, xs + (size_t)t * KB + lo * 4, ns * 4, lane);
+    }
+    if (mine()) dense_run<4>(wsb, s + (size_t)(n0 / 32) * KB + lo * 4, ns * 4, lane);
+    if (mine()) dense_run<4>(wsb + SL, s + (size_t)(n0 / 32 + 1) * KB + lo * 4, ns * 4, lane);
+  }
+  const uint8_t* wrow = w + (size_t)(n0 + 16 * wave + r16) * K;
+  const int nt = (M + 15) / 16;   // 16-token groups (the MFMA's B columns)
+  f32x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 A0[4], A1[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ks = lo + min(u, ns - 1);
+    A0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
+    A1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int j0 = 0; j0 < ns; j0 += 4) {
+    u32x4 B0[4], B1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + 4 + u < ns) {
+        const int ks = lo + j0 + 4 + u;
+        B0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
+        B1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      if (j < ns) {
+        const i32x8 Af = i32x8{(int)A0[u][0], (int)A0[u][1], (int)A0[u][2], (int)A0[u][3],
+                               (int)A1[u][0], (int)A1[u][1], (int)A1[u][2], (int)A1[u][3]};
+        const int sa = wsb[(wave >> 1) * SL + 4 * j + g];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < nt) {
+            const int t = min(16 * q + r16, M - 1);   // columns past M repeat the last row (discarded)
+            const u32x4 b0 = *reinterpret_cast<const u32x4*>(xb + t * RL + j * 128 + 16 * g);
+            const u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + t * RL + j * 128 + 64 + 16 * g);
+            const i32x8 Bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+            acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[q], 0, 0, 0, sa, 0,
+                                                                     (int)xsb[t * SL + 4 * j + g]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      A0[u] = B0[u];
+      A1[u] = B1[u];
+    }
+  }
+  // lane: weight rows n0 + 16 wave + 4g .. + 3 of token 16 q + r16
+  const int n = n0 + 16 * wave + 4 * g;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = 16 * q + r16;
+    if (q < nt && t < M) {
+      if (part != nullptr) {
+        *reinterpret_cast<f32x4*>(part + ((size_t)blockIdx.y * M + t) * N + n) = acc[q];
+      } else if (y32 != nullptr) {
+        *reinterpret_cast<f32x4*>(y32 + (size_t)t * N + n) = acc[q];
+      } else {
+        const uint32_t a = uint32_t(f32_to_bf16_rne(acc[q][0])) | (uint32_t(f32_to_bf16_rne(acc[q][1])) << 16);
+        const uint32_t b = uint32_t(f32_to_bf16_rne(acc[q][2])) | (uint32_t(f32_to_bf16_rne(acc[q][3])) << 16);
+        *reinterpret_cast<u32x2*>(y + (size_t)t * N + n) = u32x2{a, b};
+      }
+    }
+  }
+}
+
+// y = the runs' fp32 partial sums added in ascending run order, then bf16 (or fp32): 4 outputs per thread.
+__global__ __launch_bounds__(256) void dense_reduce_kernel(long long n4, int runs, long long stride,
+                                                           const float* __restrict__ part, uint16_t* __restrict__ y,
+                                                           float* __restrict__ y32) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(part + 4 * i);
+    for (int z = 1; z < runs; ++z) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(part + z * stride + 4 * i);
+      a = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+    }
+    if (y32 != nullptr) {
+      *reinterpret_cast<f32x4*>(y32 + 4 * i) = a;
+    } else {
+      const uint32_t lo = uint32_t(f32_to_bf16_rne(a[0])) | (uint32_t(f32_to_bf16_rne(a[1])) << 16);
+      const uint32_t hi = uint32_t(f32_to_bf16_rne(a[2])) | (uint32_t(f32_to_bf16_rne(a[3])) << 16);
+      *reinterpret_cast<u32x2*>(y + 4 * i) = u32x2{lo, hi};
+    }
+  }
+}
+
+DensePlan dense_plan(int M, int N, int K) {
+  DensePlan pl{};
+  const int nk = K / 128, cols = N / 64;
+  const int m16 = ((M + 15) / 16) * 16;
+  // LDS of one run: activation codes and scales of the M rows plus two weight-scale rows, within 48 KB
+  const int max_steps = std::max(1, 49152 / (m16 * 132 + 8));
+  int runs = std::max(1, std::min(nk, (1024 + cols - 1) / cols));   // about 1024 blocks
+  int spr = (nk + runs - 1) / runs;
+  spr = std::min(std::max(spr, 2), max_steps);
+  spr = std::min(spr, nk);
+  runs = (nk + spr - 1) / spr;
+  pl.runs = runs;
+  pl.steps_per_run = spr;
+  pl.lds = (size_t)M * spr * 132 + 2 * spr * 4;
+  return pl;
+}
+
+void launch_fp8_linear_stream(int M, int N, int K, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
+                              const uint8_t* s, float* part, uint16_t* y, float* y32, hipStream_t st) {
+  const DensePlan pl = dense_plan(M, N, K);
+  dim3 grid(N / 64, pl.runs);
+  if (pl.runs > 1) {
+    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, xq, xs, w, s, part, nullptr,
+                                                       nullptr);
+    const long long n4 = (long long)M * N / 4;
+    const int rg = (int)std::min<long long>((n4 + 255) / 256, 4096);
+    dense_reduce_kernel<<<dim3(rg), dim3(256), 0, st>>>(n4, pl.runs, (long long)M * N, part, y, y32);
+  } else {
+    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, xq, xs, w, s, nullptr, y, y32);
+  }
+}
+
+}  // namespace moe

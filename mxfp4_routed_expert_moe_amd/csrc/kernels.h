@@ -107,6 +107,21 @@ void launch_combine_official_f32(int M, int H, int k, const int32_t* ids, const 
                                  const float* shared_f32, const uint16_t* shared_bf16, uint16_t* out, hipStream_t s);
 void launch_combine_sum_f32(int M, int H, int k, const int32_t* ids, const float* slot_f32, const float* add,
                             float* out, hipStream_t s);
+// ---- dense FP8 linear (dense.hip) ----------------------------------------------------------
+// Per-32 E4M3 QDQ of every row of x [M, K].
+void launch_qdq_rows(int M, int K, const uint16_t* x, uint8_t* xq, uint8_t* xs, hipStream_t s);
+// Decode-width plan: the K steps are split into runs of steps_per_run (one block column per run); lds =
+// dynamic LDS bytes per block. runs > 1 needs fp32 partials [runs, M, N].
+struct DensePlan {
+  int runs;
+  int steps_per_run;
+  size_t lds;
+};
+DensePlan dense_plan(int M, int N, int K);
+// y = bf16(x_hat W^T) (or fp32 into y32) for M <= 64: W FP8 [N, K] with E8M0 [N/32, K/32]; N % 64 == 0.
+void launch_fp8_linear_stream(int M, int N, int K, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
+                              const uint8_t* s, float* part, uint16_t* y, float* y32, hipStream_t st);
+
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,
                     const uint16_t* shared_out, uint16_t* out, hipStream_t s);
 

@@ -513,6 +513,76 @@ moe_status moe_combine_official_f32(const moe_dims* dims, int32_t M, const int32
   return launched();
 }
 
+// ---- dense FP8 linear -------------------------------------------------------------------------
+namespace {
+
+moe_status check_linear(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0 || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (M > (1 << 24) || (int64_t)M * K > (int64_t(1) << 31) || (int64_t)M * N > (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct LinearLayout {
+  size_t xq, xs, part, total;
+};
+
+LinearLayout linear_layout(int32_t M, int32_t N, int32_t K) {
+  LinearLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes, 256);
+    return o;
+  };
+  const size_t m = (size_t)M;
+  L.xq = take(m * K);
+  L.xs = take(m * K / 32);
+  size_t part = 0;
+  if (M > 0 && M <= 64) {
+    const moe::DensePlan pl = moe::dense_plan(M, N, K);
+    if (pl.runs > 1) part = (size_t)pl.runs * m * N * 4;
+  }
+  L.part = take(part);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t moe_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (check_linear(M, N, K) != MOE_OK) return 0;
+  return std::max<size_t>(linear_layout(M, N, K).total, 256);
+}
+
+moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, const uint8_t* s,
+                          uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_linear(M, N, K));
+  if ((y == nullptr) == (y_f32 == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!al(x, 16) || !al(w, 16) || !al(s, 16) || !al(ws, 256)) return MOE_ERR_INVALID_ARG;
+  if ((y != nullptr && !al(y, 16)) || (y_f32 != nullptr && !al(y_f32, 16))) return MOE_ERR_INVALID_ARG;
+  const LinearLayout L = linear_layout(M, N, K);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* xq = at<uint8_t>(ws, L.xq);
+  uint8_t* xs = at<uint8_t>(ws, L.xs);
+  moe::launch_qdq_rows(M, K, x, xq, xs, st);
+  if (M <= 64) {
+    moe::launch_fp8_linear_stream(M, N, K, xq, xs, w, s, at<float>(ws, L.part), y, y_f32, st);
+  } else {
+    GemmProblem q{};
+    q.dense = 1; q.M = M; q.k = 1; q.num_experts = 1;
+    q.wa = w; q.sa = s; q.w_expert_stride = 0; q.s_expert_stride = 0;
+    q.N = N; q.K = K;
+    q.act_q = xq; q.act_s = xs; q.act_by_token = 0;
+    q.out = y; q.out_f32 = y_f32;
+    moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, nullptr, nullptr, nullptr, st);
+  }
+  return launched();
+}
+
 size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims) {
   if (check_dims(dims, 0) != MOE_OK) return 0;
   return stage_scales_off(dims, 3);

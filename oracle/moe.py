@@ -189,6 +189,19 @@ def shared_weights(inp: dict):
 
 
 # ----------------------------------------------------------------------------------------------
+# dense FP8 linear (section 4, "Dense")
+# ----------------------------------------------------------------------------------------------
+def fp8_linear(x_bits: np.ndarray, w: np.ndarray, s: np.ndarray) -> dict:
+    """y = bf16(act_qdq(x) W^T): the page's dense projection family, W FP8 E4M3 [N, K] with one E8M0
+    per 32x32 block ``s`` [N/32, K/32], x bf16 bits [M, K] QDQ'd per 32 along K (section 2
+    "Quantized linear"). Returns the QDQ codes and scales, the exact sums ``acc`` (fp64) and y (fp64
+    values of bf16)."""
+    xq, xs, xhat = act_qdq(F.bf16_from_bits(x_bits))
+    acc = xhat @ F.decode_fp8_blocks(w, s).T
+    return dict(xq=xq, xs=xs, acc=acc, y=F.bf16_rne(acc))
+
+
+# ----------------------------------------------------------------------------------------------
 # combine (section 2, "MoE") and the whole layer
 # ----------------------------------------------------------------------------------------------
 def combine(ids: np.ndarray, slot_y: np.ndarray, shared_y: np.ndarray | None) -> np.ndarray:

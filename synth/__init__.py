@@ -142,6 +142,26 @@ def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
     return out
 
 
+# The dense FP8 projection family of the native-tensor page (section 4 "Dense"), N x K per rank.
+DENSE_SHAPES = {
+    "wq_a": (1280, 5120),
+    "wkv": (512, 5120),
+    "wq_b": (16384, 1280),
+    "wo_b": (5120, 4096),
+    "main_proj": (5120, 15360),
+}
+
+
+def make_dense_inputs(N: int, K: int, M: int, seed: int = 7) -> dict:
+    """One dense FP8 linear: x bf16 bits [M, K] = RNE(N(0, 1)); w uniform over the finite E4M3 codes
+    [N, K]; s E8M0 uniform in [118, 124] per 32x32 block [N/32, K/32]. Draw order: x, w, s."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = _finite_e4m3_bytes(rng, (N, K))
+    s = rng.integers(118, 125, size=(N // 32, K // 32), dtype=np.uint8)
+    return dict(x=x, w=w, s=s)
+
+
 def digest(inputs: dict) -> dict:
     """sha256 of every generated tensor (recorded beside results)."""
     return {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16]

@@ -161,3 +161,32 @@ def test_permute_is_a_stable_counting_sort():
     assert np.array_equal(p["pairs"][p["inv"].reshape(-1)], np.arange(flat.size))
     act = p["active"][: p["n_active"]]
     assert np.array_equal(act, np.unique(flat)) and np.all(p["active"][p["n_active"]:] == -1)
+
+
+def test_fp8_linear_one_hot_closed_form():
+    """One nonzero E4M3 code c at (n, k) with block scale b: y[:, n] = bf16(xhat[:, k] * e4m3(c) * 2^(b-127)),
+    every other output 0 (fingerprints the row/column roles and the 32x32 scale indexing)."""
+    N, K = 96, 160
+    for n, k, c, b in ((0, 0, 0x38, 127), (70, 131, 0xC9, 121), (95, 159, 0x7E, 124)):
+        w = np.zeros((N, K), dtype=np.uint8)
+        w[n, k] = c
+        s = np.full((N // 32, K // 32), 127, dtype=np.uint8)
+        s[n // 32, k // 32] = b
+        x = synth.make_dense_inputs(N, K, 3, seed=n + k)["x"]
+        o = moe.fp8_linear(x, w, s)
+        _, _, xhat = moe.act_qdq(F.bf16_from_bits(x))
+        want = F.bf16_rne(xhat[:, k] * F.e4m3_decode(np.array([c]))[0] * 2.0 ** (b - 127))
+        assert np.array_equal(o["y"][:, n], want)
+        assert np.count_nonzero(np.delete(o["y"], n, axis=1)) == 0
+
+
+def test_fp8_linear_equals_exact_integer_sums():
+    """Sampled outputs of a full-size projection (wo_b, K = 4096) against exact integer dot products."""
+    N, K = 256, 4096
+    inp = synth.make_dense_inputs(N, K, 2, seed=11)
+    o = moe.fp8_linear(inp["x"], inp["w"], inp["s"])
+    for t in range(2):
+        _, _, xdeq = exact.qdq_row([float(v) for v in F.bf16_from_bits(inp["x"][t])])
+        for n in (0, 31, 32, 255):
+            row = exact.fp8_row(inp["w"][n], inp["s"][n // 32])
+            assert exact.to_bf16(exact.dot_fixed(xdeq, row)) == o["y"][t, n]
