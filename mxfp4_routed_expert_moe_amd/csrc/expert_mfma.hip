@@ -438,6 +438,232 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
   }
 }
 
+// =================================================================================================
+// MXFP4 variant with the weights streamed straight into registers. Each weight row is used by exactly
+// one wave (wave tile: 64 weight rows x the block's 128 activation rows), so the weights need no LDS:
+// every lane loads its own 16-byte MX blocks (one per 16-row fragment per 128-wide K step), as the
+// MFMA's A operand wants them. Only the activation tile (128 rows x 128 E4M3 bytes per step, shared by
+// the four waves) and the E8M0 bytes of the step go through a three-slot LDS ring of direct copies,
+// 17.5 KB per slot, so two blocks fit on a CU: one block's epilogue overlaps the other's matrix work.
+// GEMM1: wave w holds w1 rows n0 + 32 w .. + 31 (fragments 0, 1) and the same rows of w3 (fragments 2, 3),
+// so a SwiGLU pair and a 32-column QDQ block meet in one lane; the block covers 128 output columns.
+// GEMM2: wave w holds w2 rows n0 + 64 w .. + 63; the block covers 256 output columns.
+// =================================================================================================
+namespace {
+
+constexpr int kDaStages = 3;
+struct DaStage {
+  uint8_t a[kTileM * kStepK];   // activation codes, 128-byte rows, chunks swizzled
+  uint8_t ws[256 * 4];          // weight scales, row 64 w + 16 a + r16 of fragment a of wave w
+  uint8_t as[kTileM * 4];       // activation scales
+};
+
+}  // namespace
+
+template <bool GEMM1>
+__global__ __launch_bounds__(256, 2) void expert_gemm_mfma_da(GemmProblem p, const int32_t* __restrict__ tile_e,
+                                                              const int32_t* __restrict__ tile_r0,
+                                                              const int32_t* __restrict__ info) {
+  __shared__ __align__(16) DaStage ring[kDaStages];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int C = GEMM1 ? p.N / 128 : (p.N + 255) / 256;                     // column tiles
+  const int RT = info[0];                                                   // row tiles
+  const int W = RT * C;
+  const int L = blockIdx.x;
+  if (L >= W) return;
+  int w = L / 8;
+  for (int i = 0; i < L % 8; ++i) w += (W - i + 7) / 8;   // blocks of the XCDs before this one
+  const int ew = tile_e[w / C];
+  const int first = info[1 + ew], nt = info[1 + p.num_experts + ew];
+  const int local = w - first * C;
+  const int cx = local / nt, ty = first + local % nt;
+  const int e = tile_e[ty];
+  const int row0 = tile_r0[ty];
+  const int nrows = min(kTileM, p.offsets[e + 1] - row0);
+  const int K = p.K, KB = K / 32, nk = K / kStepK;
+  const int n0 = cx * (GEMM1 ? 128 : 256);
+  // global row of fragment a (0..3), row r of this wave
+  auto grow = [&](int a, int r) {
+    if constexpr (GEMM1) return n0 + 32 * wave + 16 * (a & 1) + r;
+    else return min(n0 + 64 * wave + 16 * a + r, p.N - 1);
+  };
+  // weight rows: a wave-uniform base per matrix plus a 32-bit lane offset per fragment (an expert
+  // matrix is N * K / 2 < 2^31 bytes)
+  const uint8_t* wbase_a = static_cast<const uint8_t*>(p.wa) + (size_t)e * p.w_expert_stride;
+  const uint8_t* wbase_b = GEMM1 ? static_cast<const uint8_t*>(p.wb) + (size_t)e * p.w_expert_stride : wbase_a;
+  uint32_t aoff[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) aoff[a] = (uint32_t)grow(a, r16) * (uint32_t)(K / 2) + 16u * g;
+  // per-stage copies: activation rows (4 of 8 rows x 128 B per wave), weight scales (the wave's 64 rows,
+  // 4 bytes each), activation scales (32 rows per wave, 4 bytes each)
+  auto act_row = [&](int t) {
+    const int pos = row0 + (t < nrows ? t : 0);
+    return (p.act_by_token && !p.dense) ? p.pairs[pos] / p.k : pos;
+  };
+  const uint8_t* asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = wave * 32 + i * 8 + lane / 8;
+    const int gc = (lane % 8) ^ chunk_key<kStepK>(t);
+    asrc[i] = p.act_q + (size_t)act_row(t) * K + gc * 16;
+  }
+  const size_t ws_step = p.s_stage_major ? (size_t)p.N * 4 : 4;
+  const uint8_t* wssrc;
+  {
+    const int a = lane >> 4;
+    const uint8_t* sb = (GEMM1 && a >= 2) ? p.sb : p.sa;
+    wssrc = sb + (size_t)e * p.s_expert_stride + (size_t)grow(a, r16) * (p.s_stage_major ? 4 : KB);
+  }
+  const uint8_t* assrc;
+  size_t as_step = 4;
+  {
+    const int t = wave * 32 + (lane & 31);
+    if (p.a_stage_major) {
+      assrc = p.act_s + (size_t)(row0 + (t < nrows ? t : 0)) * 4;
+      as_step = (size_t)p.M * p.k * 4;
+    } else {
+      assrc = p.act_s + (size_t)act_row(t) * KB;
+    }
+  }
+  auto issue_lds = [&](int s) {
+    DaStage& st = ring[s % kDaStages];
+    const int k0 = s * kStepK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + k0, &st.a[(wave * 32 + i * 8) * kStepK]);
+    dma4(wssrc + (size_t)s * ws_step, &st.ws[wave * 64 * 4]);
+    if (lane < 32) dma4(assrc + (size_t)s * as_step, &st.as[wave * 32 * 4]);
+  };
+  auto load_a = [&](u32x4 (&A)[4], int s) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      A[a] = *reinterpret_cast<const u32x4*>(((GEMM1 && a >= 2) ? wbase_b : wbase_a) + aoff[a] + s * (kStepK / 2));
+  };
+
+  // B fragments of this wave's 128 rows that hold a row of the tile (the last tile of an expert is partial)
+  const int nbv = min(8, (nrows + 15) / 16);
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const u32x4 (&A)[4], int s, auto part) {
+    constexpr bool PART = decltype(part)::value;
+    const DaStage& st = ring[s % kDaStages];
+    int sa[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) sa[a] = st.ws[(wave * 64 + 16 * a + r16) * 4 + g];
+    i32x8 Af[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) Af[a] = i32x8{(int)A[a][0], (int)A[a][1], (int)A[a][2], (int)A[a][3], 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (!PART || b < nbv) {
+        const int t = 16 * b + r16;
+        const int key = chunk_key<kStepK>(t);
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * (g ^ key)]);
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(&st.a[t * kStepK + 16 * ((4 + g) ^ key)]);
+        const int sb = st.as[t * 4 + g];
+        const i32x8 Bf = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2],
+                               (int)b1[3]};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af[a], Bf, acc[a][b], kFmtFp4, kFmtFp8, 0,
+                                                                       sa[a], 0, sb);
+      }
+    }
+    // schedule: the three LDS reads of fragment b, then its four MFMAs (keeps one B fragment live)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  };
+  // Issue order: at step s the weight blocks of step s + 1 (4 loads into registers), then the LDS copies
+  // of step s + 2 (6: 4 activation, 1 weight-scale, 1 activation-scale), then the MFMAs of step s. So
+  // before step s only the copies of step s + 1 may still be in flight: vmcnt(6) (0 near the end).
+  auto wait_stage = [&](int s) {
+    if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  u32x4 A0[4], A1[4];
+  issue_lds(0);
+  load_a(A0, 0);
+  if (nk > 1) issue_lds(1);
+  // (the last, partial row tile of an expert runs a copy of the loop that skips its empty 16-row
+  // activation fragments; full tiles run a copy without the checks)
+  auto kloop = [&](auto part) {
+    for (int s = 0; s < nk; ++s) {
+      wait_stage(s);
+      if (s + 1 < nk) load_a(A1, s + 1);
+      if (s + 2 < nk) issue_lds(s + 2);
+      compute(A0, s, part);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) A0[a] = A1[a];
+    }
+  };
+  if (nbv == 8) kloop(kFull);
+  else kloop(kPartial);
+
+  // ---- epilogue: lane holds weight rows 4g..4g+3 of each A fragment for activation row r16 of each B
+  // fragment
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int tt = 16 * b + r16;
+    const bool valid = tt < nrows;
+    const int pos = row0 + tt;
+    if constexpr (GEMM1) {
+      float rwv = 1.0f;
+      if (valid) rwv = p.rw[p.pairs[pos]];
+      float h[2][4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gv = round_bf16(acc[half][b][v]);
+          const float uv = round_bf16(acc[2 + half][b][v]);
+          h[half][v] = round_bf16(swiglu(gv, uv, rwv, true));
+          amax = fmaxf(amax, fabsf(h[half][v]));
+        }
+      // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int E8 = qdq_exponent(amax);
+      const float inv = exp2_neg(E8);
+      if (valid) {
+        const int col0 = n0 + 32 * wave;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t packed = qdq_code4(h[half][0], h[half][1], h[half][2], h[half][3], inv);
+          *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + col0 + 16 * half + 4 * g) = packed;
+        }
+        if (g == 0) {
+          const size_t at = p.h_s_stage_major ? ((size_t)(col0 / 128) * p.M * p.k + pos) * 4 + (col0 / 32) % 4
+                                              : (size_t)pos * (p.N / 32) + col0 / 32;
+          p.h_s[at] = uint8_t(E8 + 127);
+        }
+      }
+    } else {
+      if (valid && n0 + 64 * wave < p.N) {
+        const int orow = p.pairs[pos];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int col = n0 + 64 * wave + 16 * a + 4 * g;
+          if (p.out_f32) {
+            *reinterpret_cast<f32x4*>(p.out_f32 + (size_t)orow * p.N + col) = acc[a][b];
+          } else {
+            const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[a][b][0])) | (uint32_t(f32_to_bf16_rne(acc[a][b][1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[a][b][2])) | (uint32_t(f32_to_bf16_rne(acc[a][b][3])) << 16);
+            *reinterpret_cast<u32x2*>(p.out + (size_t)orow * p.N + col) = u32x2{lo, hi};
+          }
+        }
+      }
+    }
+  }
+}
+
 // One block per 64 rows of one matrix: the rows' scale bytes go through LDS (coalesced dword reads
 // along the rows, coalesced dword writes along the stage-major rows).
 __global__ __launch_bounds__(256) void scales_stage_major_kernel(int N, int KB, const uint8_t* __restrict__ s,
@@ -497,8 +723,13 @@ static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, con
                         const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
   switch (f) {
     case W_MXFP4:
-      if (!GEMM1 || p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 512>(p, max_tiles, tile_e, tile_r0, info, s);
-      else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
+      if constexpr (GEMM1) {   // long K: the 512-row LDS ring streams best
+        if (p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 512>(p, max_tiles, tile_e, tile_r0, info, s);
+        else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
+      } else {   // short K: weights straight into registers, two blocks per CU overlap their epilogues
+        expert_gemm_mfma_da<false><<<dim3(((p.N + 255) / 256) * max_tiles), dim3(256), 0, s>>>(p, tile_e, tile_r0,
+                                                                                               info);
+      }
       break;
     case W_FP8_BLOCK32: launch_mfma_tn<W_FP8_BLOCK32, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s); break;
     default: break;   // the bf16 arm has no block-scaled form; the caller never asks for it here
