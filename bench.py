@@ -187,7 +187,34 @@ def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
     gemm1_bytes = D * w13_b + cfg.M * (cfg.H + cfg.H // 32) + P * (cfg.I + cfg.I // 32)
     gemm1_flops = P * f13
     layer_bytes = D * (w13_b + w2_b) + cfg.E * cfg.H * 4
+    # the same steps replayed from a HIP graph (one capture of R steps, one per weight replica): no host
+    # launch work between the kernels
+    R = len(L.experts)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(R):
+            L.step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(R):
+            L.step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, steps // R)
+    g0, g1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(n_rep):
+        graph.replay()
+    g1e.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1e) / (n_rep * R)
+    del graph
+
     res = dict(workload=cfg.name, M=cfg.M, ms_per_step=ms, tokens_per_s=cfg.M / (ms * 1e-3), distinct_experts=D,
+               graph_ms_per_step=graph_ms,
                kernel_us=kern_us, layer_weight_bytes=layer_bytes,
                layer_hbm_frac=(layer_bytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9),
                layer_tflops=(P * (f13 + f2)) / (ms * 1e-3) / 1e12, replicas=replicas, inputs_sha256=L.digest)
@@ -322,7 +349,8 @@ def main():
         print(json.dumps({"calibrate_copy": calibrate_copy()}), flush=True)
         return
     main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas)
-    print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step, kernels {main_res['kernel_us']}",
+    print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step "
+          f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f}), kernels {main_res['kernel_us']}",
           file=sys.stderr, flush=True)
     prefill = None
     if not args.no_prefill and args.workload != "prefill_m8192":
@@ -332,6 +360,7 @@ def main():
         prefill = dict(workload=p["workload"], value=round(p["tokens_per_s"], 1), unit="tokens/s",
                        ms_per_step=round(p["ms_per_step"], 4), kernel_us={k: round(v, 1) for k, v in
                                                                           p["kernel_us"].items()},
+                       graph_ms_per_step=round(p["graph_ms_per_step"], 4),
                        layer_tflops=round(p["layer_tflops"], 1), roofline=p["roofline"])
     dense = None
     if not args.no_dense:
@@ -358,6 +387,7 @@ def main():
         "config": {"workload": r["workload"], "M": r["M"], "hidden": 5120, "experts": 128, "inter": 2304,
                    "top_k": 6, "distinct_experts": r["distinct_experts"], "weight_replicas": r["replicas"],
                    "parallelism": "none (1 GPU)"},
+        "graph_ms_per_step": round(r["graph_ms_per_step"], 5),
         "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()},
         "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
         "roofline": r["roofline"],
