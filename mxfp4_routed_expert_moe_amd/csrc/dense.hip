@@ -6,7 +6,7 @@
 // the inner dimension split across blocks so that even N = 512 fills the chip. Block (c, z) owns 64
 // weight rows (one 16-row fragment per wave) and the z-th run of 128-wide K steps; the M activation
 // rows of that run (E4M3 codes and scales) and the two 32-row weight-scale rows are copied into LDS
-// once. The partial sums of the runs are added in ascending run order by a second kernel (fp32, then
+// once (or, given the bf16 rows, QDQ'd straight into LDS by the block). The partial sums of the runs are added in ascending run order by a second kernel (fp32, then
 // bf16 or fp32 out). Wider batches use the prefill-width grouped GEMM as a single expert.
 //
 // Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E4M3 operand holds K
@@ -52,6 +52,7 @@ __device__ __forceinline__ void dense_run(uint8_t* lds, const uint8_t* src, int 
 // Dynamic LDS: activation codes [M][S * 128], activation scales [M][S * 4], weight scales [2][S * 4]
 // (S = steps of this run).
 __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, int steps_per_run,
+                                                         const uint16_t* __restrict__ x,
                                                          const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                                                          const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
                                                          float* __restrict__ part, uint16_t* __restrict__ y,
@@ -69,13 +70,16 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
   {
     int run = 0;
     auto mine = [&]() { return (run++ & 3) == wave; };
-    for (int t = 0; t < M; ++t) {
-      if (mine()) dense_run<16>(xb + t * RL, xq + (size_t)t * K + lo * 128, ns * 128, lane);
-      if (mine()) dense_run<4>(xsb + t * SL, xs + (size_t)t * KB + lo * 4, ns * 4, lane);
+    if (x == nullptr) {   // QDQ'd rows given: copy this run's codes and scales
+      for (int t = 0; t < M; ++t) {
+        if (mine()) dense_run<16>(xb + t * RL, xq + (size_t)t * K + lo * 128, ns * 128, lane);
+        if (mine()) dense_run<4>(xsb + t * SL, xs + (size_t)t * KB + lo * 4, ns * 4, lane);
+      }
     }
     if (mine()) dense_run<4>(wsb, s + (size_t)(n0 / 32) * KB + lo * 4, ns * 4, lane);
     if (mine()) dense_run<4>(wsb + SL, s + (size_t)(n0 / 32 + 1) * KB + lo * 4, ns * 4, lane);
   }
+  // the first weight steps are in flight while the activations are staged
   const uint8_t* wrow = w + (size_t)(n0 + 16 * wave + r16) * K;
   const int nt = (M + 15) / 16;   // 16-token groups (the MFMA's B columns)
   f32x4 acc[4];
@@ -87,6 +91,17 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
     const int ks = lo + min(u, ns - 1);
     A0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
     A1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
+  }
+  if (x != nullptr) {   // bf16 rows given: QDQ this run's 32-wide blocks straight into LDS (thread per block)
+    const int nb = ns * 4;
+    for (int i = threadIdx.x; i < M * nb; i += 256) {
+      const int t = i / nb, j = i % nb;
+      u32x4 q0, q1;
+      const uint8_t sc = qdq_block32_regs(x + (size_t)t * K + lo * 128 + j * 32, q0, q1);
+      *reinterpret_cast<u32x4*>(xb + t * RL + j * 32) = q0;
+      *reinterpret_cast<u32x4*>(xb + t * RL + j * 32 + 16) = q1;
+      xsb[t * SL + j] = sc;
+    }
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   for (int j0 = 0; j0 < ns; j0 += 4) {
@@ -181,18 +196,19 @@ DensePlan dense_plan(int M, int N, int K) {
   return pl;
 }
 
-void launch_fp8_linear_stream(int M, int N, int K, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
-                              const uint8_t* s, float* part, uint16_t* y, float* y32, hipStream_t st) {
+void launch_fp8_linear_stream(int M, int N, int K, const uint16_t* x, const uint8_t* xq, const uint8_t* xs,
+                              const uint8_t* w, const uint8_t* s, float* part, uint16_t* y, float* y32,
+                              hipStream_t st) {
   const DensePlan pl = dense_plan(M, N, K);
   dim3 grid(N / 64, pl.runs);
   if (pl.runs > 1) {
-    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, xq, xs, w, s, part, nullptr,
+    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, part, nullptr,
                                                        nullptr);
     const long long n4 = (long long)M * N / 4;
     const int rg = (int)std::min<long long>((n4 + 255) / 256, 4096);
     dense_reduce_kernel<<<dim3(rg), dim3(256), 0, st>>>(n4, pl.runs, (long long)M * N, part, y, y32);
   } else {
-    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, xq, xs, w, s, nullptr, y, y32);
+    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, nullptr, y, y32);
   }
 }
 

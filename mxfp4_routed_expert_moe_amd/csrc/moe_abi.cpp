@@ -568,10 +568,10 @@ moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* xq = at<uint8_t>(ws, L.xq);
   uint8_t* xs = at<uint8_t>(ws, L.xs);
-  moe::launch_qdq_rows(M, K, x, xq, xs, st);
-  if (M <= 64) {
-    moe::launch_fp8_linear_stream(M, N, K, xq, xs, w, s, at<float>(ws, L.part), y, y_f32, st);
+  if (M <= 64) {   // the blocks QDQ their own runs of x
+    moe::launch_fp8_linear_stream(M, N, K, x, nullptr, nullptr, w, s, at<float>(ws, L.part), y, y_f32, st);
   } else {
+    moe::launch_qdq_rows(M, K, x, xq, xs, st);
     GemmProblem q{};
     q.dense = 1; q.M = M; q.k = 1; q.num_experts = 1;
     q.wa = w; q.sa = s; q.w_expert_stride = 0; q.s_expert_stride = 0;

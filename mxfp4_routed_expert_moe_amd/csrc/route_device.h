@@ -136,9 +136,9 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
   }
 }
 
-// QDQ of one 32-wide block of a bf16 row: 32 E4M3 codes to q (16-byte aligned) and the E8M0 byte to *s.
-__device__ __forceinline__ void qdq_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
-                                            uint8_t* __restrict__ s) {
+// QDQ of one 32-wide block of a bf16 row into registers: the 32 E4M3 codes (little-endian, 16 per
+// u32x4) and the returned E8M0 byte.
+__device__ __forceinline__ uint8_t qdq_block32_regs(const uint16_t* __restrict__ src, u32x4& q0, u32x4& q1) {
   u32x4 raw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const u32x4*>(src + 8 * i);
@@ -155,15 +155,23 @@ __device__ __forceinline__ void qdq_block32(const uint16_t* __restrict__ src, ui
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int E8 = qdq_exponent(amax);
   const float inv = exp2_neg(E8);
-  u32x4 out[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[i >> 2][i & 3] = qdq_code4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], inv);
+  for (int i = 0; i < 4; ++i) {
+    q0[i] = qdq_code4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], inv);
+    q1[i] = qdq_code4(v[16 + 4 * i], v[17 + 4 * i], v[18 + 4 * i], v[19 + 4 * i], inv);
   }
+  return uint8_t(E8 + 127);
+}
+
+// QDQ of one 32-wide block of a bf16 row: 32 E4M3 codes to q (16-byte aligned) and the E8M0 byte to *s.
+__device__ __forceinline__ void qdq_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ q,
+                                            uint8_t* __restrict__ s) {
+  u32x4 q0, q1;
+  const uint8_t sc = qdq_block32_regs(src, q0, q1);
   u32x4* dst = reinterpret_cast<u32x4*>(q);
-  dst[0] = out[0];
-  dst[1] = out[1];
-  *s = uint8_t(E8 + 127);
+  dst[0] = q0;
+  dst[1] = q1;
+  *s = sc;
 }
 
 }  // namespace moe
