@@ -37,8 +37,8 @@ WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m81
 # were measured on (sha256 prefix); after any change to it the traffic is reported as null until re-measured.
 FETCH_SCALE, WRITE_SCALE = 1048576 / 524300.9, 1.0
 MEASURED_TRAFFIC = {
-    "decode_m8": dict(src="expert_gemm.hip", sha="9032bdd39b8aba5d", fetch_kib=226983.0, write_kib=137.7),
-    "prefill_m8192": dict(src="expert_mfma.hip", sha="a9e033dda3e5e351", fetch_kib=1265446.0, write_kib=118748.4),
+    "decode_m8": dict(src="expert_gemm.hip", sha="9032bdd39b8aba5d", fetch_kib=226992.6, write_kib=137.6),
+    "prefill_m8192": dict(src="expert_mfma.hip", sha="282ab27b183d7120", fetch_kib=1258222.9, write_kib=117474.4),
 }
 
 
