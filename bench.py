@@ -147,7 +147,76 @@ class Layer:
         return int(self.torch.unique(self.ids).numel())
 
 
-def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
+VERIFIER_WIDTHS = (1, 2, 4, 5, 10, 15, 20, 32)
+
+
+def measure_widths(L: Layer, widths, steps: int, warmup: int) -> dict:
+    """The same layer weights (all replicas) at the verifier widths M: moe_forward eager over rotated
+    replicas, and the same steps replayed from a HIP graph. Token rows are the workload's own draw,
+    extended (the first rows are the decode batch's)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    moe, cfg = L.moe, L.cfg
+    Mx = max(widths)
+    xw = torch.from_numpy(synth.make_tokens(dataclasses.replace(cfg, M=Mx)).view(np.int16)).cuda()
+    dev = dict(device="cuda")
+    ws = moe.workspace(L.dims, Mx)
+    out = torch.empty((Mx, cfg.H), dtype=torch.int16, **dev)
+    ids = torch.empty((Mx, cfg.k), dtype=torch.int32, **dev)
+    rw = torch.empty((Mx, cfg.k), dtype=torch.float32, **dev)
+    R = len(L.experts)
+    w13_b, w2_b = _bytes_per_expert(cfg)
+    res = {}
+    for m in widths:
+        def step(i):
+            moe.moe_forward(L.dims, xw[:m], L.gate_w, L.gate_b, L.experts[i % R], None, L.shared, out[:m],
+                            ids[:m], rw[:m], None, ws)
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        us = float("inf")
+        for _ in range(2):   # the better of two timed passes: one host stall should not set a width's figure
+            t0 = time.perf_counter()
+            for i in range(steps):
+                step(warmup + i)
+            torch.cuda.synchronize()
+            us = min(us, (time.perf_counter() - t0) * 1e6 / steps)
+        D = int(torch.unique(ids[:m]).numel())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(R):
+                step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        n_rep = max(2, steps // R)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(n_rep):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gus = g0.elapsed_time(g1) * 1e3 / (n_rep * R)
+        del graph
+        nbytes = D * (w13_b + w2_b)
+        res[str(m)] = dict(us=round(us, 1), graph_us=round(gus, 1), tokens_per_s=round(m / (us * 1e-6), 1),
+                           distinct_experts=D, weight_hbm_frac=round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4))
+    del ws, out, ids, rw, xw
+    return res
+
+
+def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None) -> dict:
     import torch
 
     L = Layer(cid, replicas)
@@ -231,16 +300,18 @@ def measure(cid: int, steps: int, warmup: int, replicas: int) -> dict:
                                peak=MFMA_FP8_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
                                traffic=_measured_traffic(cfg.name), algorithmic_flops=gemm1_flops,
                                avg_us=round(kern_us["gemm1"], 2))
+    if widths:
+        res["widths"] = measure_widths(L, widths, steps, warmup)
     del L
     torch.cuda.empty_cache()
     return res
 
 
-def measure_dense(M: int = 8, reps: int = 40, replicas: int = 4) -> dict:
-    """The dense FP8 projection family at decode width: moe_fp8_linear per shape, with the weights in R
-    replicas (rotated, so the last-level cache cannot serve them). The calls are captured once in a HIP
-    graph (the library is graph-safe) and the replays timed with HIP events, so host launch overhead
-    does not enter the per-call time."""
+def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30) -> dict:
+    """The dense FP8 projection family at decode width: moe_fp8_linear per shape, with the weights in as
+    many replicas as fill about 1 GiB (rotated, so the 256 MB last-level cache cannot serve them). The
+    calls are captured once in a HIP graph (the library is graph-safe) and the replays timed with HIP
+    events, so host launch overhead does not enter the per-call time."""
     import numpy as np
     import torch
 
@@ -251,17 +322,19 @@ def measure_dense(M: int = 8, reps: int = 40, replicas: int = 4) -> dict:
     for name, (N, K) in synth.DENSE_SHAPES.items():
         inp = synth.make_dense_inputs(N, K, M)
         x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
-        ws_ = [(torch.from_numpy(inp["w"]).cuda(), torch.from_numpy(inp["s"]).cuda()) for _ in range(replicas)]
+        replicas = max(4, -(-pool_bytes // (N * K)))
+        w0, s0 = torch.from_numpy(inp["w"]).cuda(), torch.from_numpy(inp["s"]).cuda()
+        ws_ = [(w0.clone(), s0.clone()) for _ in range(replicas)]
         y = torch.empty((M, N), dtype=torch.int16, device="cuda")
         work = moe.fp8_linear_workspace(M, N, K)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for i in range(2 * replicas):
+            for i in range(replicas):
                 moe.moe_fp8_linear(x, *ws_[i % replicas], y=y, ws=work)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        per_graph = 2 * replicas
+        per_graph = replicas
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(per_graph):
@@ -269,7 +342,7 @@ def measure_dense(M: int = 8, reps: int = 40, replicas: int = 4) -> dict:
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_rep = max(1, reps // per_graph)
+        n_rep = max(2, reps // per_graph)
         e0.record()
         for _ in range(n_rep):
             graph.replay()
@@ -278,9 +351,9 @@ def measure_dense(M: int = 8, reps: int = 40, replicas: int = 4) -> dict:
         us = e0.elapsed_time(e1) * 1e3 / (n_rep * per_graph)
         del graph
         nbytes = N * K + (N // 32) * (K // 32) + M * K * 2 + M * N * 2
-        out[name] = dict(N=N, K=K, us=round(us, 2), gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+        out[name] = dict(N=N, K=K, replicas=replicas, us=round(us, 2), gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
                          hbm_frac=round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4))
-        del ws_, work
+        del ws_, work, w0, s0
     torch.cuda.empty_cache()
     return dict(workload=f"dense FP8 projections at M={M}", bound="hbm", unit="GB/s", shapes=out)
 
@@ -331,6 +404,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
+    ap.add_argument("--no-widths", action="store_true", help="skip the verifier widths M = 1 .. 32")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="only the dense FP8 projection family (prints its object as the JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the rocprof byte counters)")
     args = ap.parse_args()
@@ -348,10 +424,17 @@ def main():
     if args.calibrate_copy:
         print(json.dumps({"calibrate_copy": calibrate_copy()}), flush=True)
         return
-    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas)
+    if args.dense_only:
+        print(json.dumps({"dense_fp8": measure_dense()}), flush=True)
+        return
+    widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
+    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths)
     print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step "
           f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f}), kernels {main_res['kernel_us']}",
           file=sys.stderr, flush=True)
+    if main_res.get("widths"):
+        print("# widths: " + ", ".join(f"M={m}: {v['us']} us ({v['distinct_experts']} experts)"
+                                       for m, v in main_res["widths"].items()), file=sys.stderr, flush=True)
     prefill = None
     if not args.no_prefill and args.workload != "prefill_m8192":
         p = measure(3, max(3, args.steps // 10), max(1, args.warmup // 5), 2)
@@ -392,6 +475,7 @@ def main():
         "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
         "roofline": r["roofline"],
         "prefill": prefill,
+        "verifier_widths": main_res.get("widths"),
         "dense_fp8": dense,
         "cpu_baseline": cpu,
     }

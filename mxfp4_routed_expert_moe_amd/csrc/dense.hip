@@ -35,6 +35,10 @@ void launch_qdq_rows(int M, int K, const uint16_t* x, uint8_t* xq, uint8_t* xs, 
 
 namespace {
 
+constexpr int kDenseInFlight = 2;       // K steps of weight loads in flight per wave (2 beat 3, 4 and 8)
+constexpr int kDenseBlocks = 1024;      // blocks the K split aims for
+constexpr int kDenseMinSteps = 4;       // fewest K steps per run
+
 // copy of a run of nbytes (a multiple of UNIT) straight into LDS by one wave
 template <int UNIT>
 __device__ __forceinline__ void dense_run(uint8_t* lds, const uint8_t* src, int nbytes, int lane) {
@@ -85,9 +89,10 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
   f32x4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 A0[4], A1[4];
+  constexpr int U = kDenseInFlight;
+  u32x4 A0[U], A1[U];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int ks = lo + min(u, ns - 1);
     A0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
     A1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
@@ -104,17 +109,17 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
     }
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int j0 = 0; j0 < ns; j0 += 4) {
-    u32x4 B0[4], B1[4];
+  for (int j0 = 0; j0 < ns; j0 += U) {
+    u32x4 B0[U], B1[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j0 + 4 + u < ns) {
-        const int ks = lo + j0 + 4 + u;
+    for (int u = 0; u < U; ++u)
+      if (j0 + U + u < ns) {
+        const int ks = lo + j0 + U + u;
         B0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
         B1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
       }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
       if (j < ns) {
         const i32x8 Af = i32x8{(int)A0[u][0], (int)A0[u][1], (int)A0[u][2], (int)A0[u][3],
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       A0[u] = B0[u];
       A1[u] = B1[u];
     }
@@ -164,10 +169,16 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(long long n4, int run
                                                            const float* __restrict__ part, uint16_t* __restrict__ y,
                                                            float* __restrict__ y32) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    // eight runs' loads in flight at a time, added in ascending run order
     f32x4 a = *reinterpret_cast<const f32x4*>(part + 4 * i);
-    for (int z = 1; z < runs; ++z) {
-      const f32x4 b = *reinterpret_cast<const f32x4*>(part + z * stride + 4 * i);
-      a = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+    for (int z0 = 1; z0 < runs; z0 += 8) {
+      f32x4 b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < runs) b[u] = *reinterpret_cast<const f32x4*>(part + (z0 + u) * stride + 4 * i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < runs) a = f32x4{a[0] + b[u][0], a[1] + b[u][1], a[2] + b[u][2], a[3] + b[u][3]};
     }
     if (y32 != nullptr) {
       *reinterpret_cast<f32x4*>(y32 + 4 * i) = a;
@@ -185,9 +196,9 @@ DensePlan dense_plan(int M, int N, int K) {
   const int m16 = ((M + 15) / 16) * 16;
   // LDS of one run: activation codes and scales of the M rows plus two weight-scale rows, within 48 KB
   const int max_steps = std::max(1, 49152 / (m16 * 132 + 8));
-  int runs = std::max(1, std::min(nk, (1024 + cols - 1) / cols));   // about 1024 blocks
+  int runs = std::max(1, std::min(nk, (kDenseBlocks + cols - 1) / cols));
   int spr = (nk + runs - 1) / runs;
-  spr = std::min(std::max(spr, 2), max_steps);
+  spr = std::min(std::max(spr, kDenseMinSteps), max_steps);
   spr = std::min(spr, nk);
   runs = (nk + spr - 1) / spr;
   pl.runs = runs;

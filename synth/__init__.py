@@ -27,7 +27,7 @@ from dataclasses import dataclass, field, asdict
 
 import numpy as np
 
-__all__ = ["LayerConfig", "CONFIGS", "get_config", "make_inputs", "digest", "c4_hot_bias"]
+__all__ = ["LayerConfig", "CONFIGS", "get_config", "make_inputs", "make_tokens", "digest", "c4_hot_bias"]
 
 
 @dataclass(frozen=True)
@@ -105,17 +105,28 @@ def _finite_e4m3_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     return v.astype(np.uint8)
 
 
-def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
-    """Draw every input tensor of one layer invocation (numpy arrays, host memory)."""
-    rng = np.random.Generator(np.random.PCG64(cfg.seed))
-    M, H, E, I = cfg.M, cfg.H, cfg.E, cfg.I
+def _draw_tokens(rng: np.random.Generator, cfg: LayerConfig):
+    M, H = cfg.M, cfg.H
     x32 = rng.standard_normal((M, H), dtype=np.float32)
     hot_rows = np.zeros(0, dtype=np.int64)
     if cfg.hot_row_frac > 0:
         n_hot = int(round(cfg.hot_row_frac * M))
         hot_rows = np.sort(rng.choice(M, size=n_hot, replace=False))
         x32[hot_rows] *= np.float32(cfg.hot_row_mult)   # power of two: exact after bf16 rounding too
-    x = _to_bf16_bits(x32)
+    return _to_bf16_bits(x32), hot_rows
+
+
+def make_tokens(cfg: LayerConfig) -> np.ndarray:
+    """Only the token rows x (bf16 bits [M, H]) of make_inputs(cfg), drawn the same way. Without hot rows,
+    the first m rows for M = m' > m equal the rows for M = m (the normal draws fill x row by row)."""
+    return _draw_tokens(np.random.Generator(np.random.PCG64(cfg.seed)), cfg)[0]
+
+
+def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
+    """Draw every input tensor of one layer invocation (numpy arrays, host memory)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    M, H, E, I = cfg.M, cfg.H, cfg.E, cfg.I
+    x, hot_rows = _draw_tokens(rng, cfg)
     gate_w = (rng.standard_normal((E, H)) * cfg.gate_std).astype(np.float32)
     gate_b = rng.uniform(-cfg.bias_half, cfg.bias_half, size=E).astype(np.float32)
     hot_experts = np.zeros(0, dtype=np.int64)
