@@ -10,7 +10,7 @@ sums stay inside fp64's 53 bits for these formats and ranges (pinned against the
 ``oracle.exact``). The steps the page fixes in fp32 (router logits, scores, normalisation, SwiGLU) are
 emulated in fp32 with correctly rounded operations.
 
-Readings of open points (each one is listed in the design doc):
+Readings of open points (where the pages leave a step open, the plainest reading the rest supports):
 * top-k order: descending selection score, ties to the lower expert id;
 * normalisation: fp32 sum of the k weights in slot order, plus 1e-20, IEEE fp32 division, times the
   route scale;
