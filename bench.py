@@ -70,7 +70,7 @@ def _flops_per_pair(cfg):
 class Layer:
     """Device-resident inputs of one workload with R weight replicas, plus output buffers."""
 
-    def __init__(self, cid: int, replicas: int):
+    def __init__(self, cid: int, replicas: int, tiled: bool = True):
         import numpy as np
         import torch
 
@@ -98,10 +98,17 @@ class Layer:
         del inp
         M, k, H, I, E = cfg.M, cfg.k, cfg.H, cfg.I, cfg.E
         self.dims = moe.Dims(E, H, I, k, cfg.route_scale)
-        # one-time re-layout of each replica's scales for the prefill-width kernels, as at weight load
+        # one-time re-layouts at weight load: each replica's scales stage-major for the prefill-width kernels,
+        # and (by default) its weight codes in fragment order, which then replace the stored row-major codes
         for w in self.experts:
             w.stage_scales = moe.moe_prepare_mxfp4_scales(self.dims, w)
+            if tiled:
+                w.tiled_weights = moe.moe_prepare_mxfp4_weights(self.dims, w)
+                torch.cuda.synchronize()
+                w.w1 = w.w3 = w.w2 = None
+        self.weight_layout = "fragment-order" if tiled else "stored row-major"
         torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         self.ws = moe.workspace(self.dims, M)
         dev = dict(device="cuda")
         self.out = torch.empty((M, H), dtype=torch.int16, **dev)
@@ -216,10 +223,10 @@ def measure_widths(L: Layer, widths, steps: int, warmup: int) -> dict:
     return res
 
 
-def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None) -> dict:
+def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled: bool = True) -> dict:
     import torch
 
-    L = Layer(cid, replicas)
+    L = Layer(cid, replicas, tiled)
     cfg = L.cfg
     for i in range(warmup):
         L.step(i)
@@ -405,6 +412,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
     ap.add_argument("--no-widths", action="store_true", help="skip the verifier widths M = 1 .. 32")
+    ap.add_argument("--stored-layout", action="store_true",
+                    help="stream the weight codes from their stored row-major layout instead of the fragment-order "
+                         "copy made at load")
     ap.add_argument("--dense-only", action="store_true",
                     help="only the dense FP8 projection family (prints its object as the JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -428,7 +438,8 @@ def main():
         print(json.dumps({"dense_fp8": measure_dense()}), flush=True)
         return
     widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
-    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths)
+    tiled = not args.stored_layout
+    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths, tiled)
     print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step "
           f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f}), kernels {main_res['kernel_us']}",
           file=sys.stderr, flush=True)
@@ -437,7 +448,7 @@ def main():
                                        for m, v in main_res["widths"].items()), file=sys.stderr, flush=True)
     prefill = None
     if not args.no_prefill and args.workload != "prefill_m8192":
-        p = measure(3, max(3, args.steps // 10), max(1, args.warmup // 5), 2)
+        p = measure(3, max(3, args.steps // 10), max(1, args.warmup // 5), 2, tiled=tiled)
         print(f"# {p['workload']}: {p['ms_per_step']:.3f} ms/step, kernels {p['kernel_us']}", file=sys.stderr,
               flush=True)
         prefill = dict(workload=p["workload"], value=round(p["tokens_per_s"], 1), unit="tokens/s",
@@ -469,6 +480,7 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": r["workload"], "M": r["M"], "hidden": 5120, "experts": 128, "inter": 2304,
                    "top_k": 6, "distinct_experts": r["distinct_experts"], "weight_replicas": r["replicas"],
+                   "weight_layout": "stored row-major" if args.stored_layout else "fragment-order",
                    "parallelism": "none (1 GPU)"},
         "graph_ms_per_step": round(r["graph_ms_per_step"], 5),
         "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()},

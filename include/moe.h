@@ -74,6 +74,10 @@ typedef struct {
    * kernels read the scales from it; without it every prefill-width call re-lays them out in the
    * workspace. */
   const uint8_t* stage_scales;
+  /* Optional (NULL = none): the output of moe_prepare_mxfp4_weights for w1, w3, w2. When given, every
+   * routed GEMM reads the weight codes from it (each 128-bit load then covers 1 KB of contiguous bytes)
+   * and w1, w3, w2 may be NULL; the scales are still read from s1, s3, s2 (and stage_scales). */
+  const uint8_t* tiled_weights;
 } moe_mxfp4_experts;
 
 /* Routed experts expanded to bf16 (section 4 "expanded weights": exactly code * 2^(b-127)). */
@@ -218,9 +222,25 @@ size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims);
  * pointers are not read (w->stage_scales is ignored). */
 moe_status moe_prepare_mxfp4_scales(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream);
 
+/* Bytes of moe_prepare_mxfp4_weights output: 3 * E * I * H / 2 (0 if dims are invalid). */
+size_t moe_mxfp4_tiled_weights_bytes(const moe_dims* dims);
+
+/* One-time re-layout of the routed experts' packed E2M1 codes (section 2 MXFP4 format: w1, w3, w2; scales
+ * untouched) into
+ * matrix-core fragment order. The values are unchanged, only their order. For each matrix m in the order
+ * w1, w3, w2 (m = [E, N, K/2] bytes: N = I, K = H for w1 and w3; N = H, K = I for w2), stored one after
+ * the other (each E * I * H / 2 bytes), out holds [E, N/16, K/128, 64, 16]:
+ *   out[e][f][q][l][b] = m[e][16 f + l % 16][64 q + 16 (l / 16) + b],
+ * i.e. fragment (f, q) is the 16 rows 16f.. by the 128 inputs 128q.. in 1024 contiguous bytes, 16 per
+ * lane l of the block-scaled matrix-core instruction (lane l: row l % 16, inputs 32 (l / 16) .. + 31).
+ * Done once (e.g. when the weights are loaded). out: device, 16-byte aligned,
+ * moe_mxfp4_tiled_weights_bytes(dims) bytes, owned by the caller; must not overlap w's weights.
+ * w's scale pointers and w->stage_scales / w->tiled_weights are not read. */
+moe_status moe_prepare_mxfp4_weights(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream);
+
 /* Expand one packed MXFP4 matrix (or a stack of them) to bf16: w uint8 [rows, cols/2], s uint8
  * [rows, cols/32] -> out bf16 [rows, cols], exactly code * 2^(b-127) (section 4 "expanded weights").
- * cols a multiple of 32, rows >= 0. */
+ * cols a multiple of 32, rows >= 0. w is in the stored row-major layout (not the tiled one). */
 moe_status moe_expand_mxfp4(int64_t rows, int32_t cols, const uint8_t* w, const uint8_t* s, uint16_t* out,
                             void* stream);
 

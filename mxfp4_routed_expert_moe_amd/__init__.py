@@ -21,6 +21,7 @@ __all__ = [
     "moe_expert_gemm1", "moe_expert_gemm2", "moe_shared_expert", "moe_combine", "moe_forward", "moe_expand_mxfp4", "workspace",
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
     "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
+    "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -43,7 +44,7 @@ class _Dims(ctypes.Structure):
 
 
 class _MXFP4(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales", "tiled_weights")]
 
 
 class _BF16(ctypes.Structure):
@@ -99,6 +100,10 @@ lib.moe_mxfp4_stage_scales_bytes.argtypes = [ctypes.POINTER(_Dims)]
 lib.moe_mxfp4_stage_scales_bytes.restype = _SZ
 lib.moe_prepare_mxfp4_scales.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
 lib.moe_prepare_mxfp4_scales.restype = _I32
+lib.moe_mxfp4_tiled_weights_bytes.argtypes = [ctypes.POINTER(_Dims)]
+lib.moe_mxfp4_tiled_weights_bytes.restype = _SZ
+lib.moe_prepare_mxfp4_weights.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
+lib.moe_prepare_mxfp4_weights.restype = _I32
 lib.moe_expand_mxfp4.argtypes = [ctypes.c_int64, _I32, _P, _P, _P, _P]
 lib.moe_expand_mxfp4.restype = _I32
 
@@ -118,17 +123,20 @@ class Dims:
 @dataclass
 class MXFP4Experts:
     """Packed routed experts: w1/w3 uint8 [E, I, H/2], s1/s3 [E, I, H/32], w2 [E, H, I/2], s2 [E, H, I/32];
-    optionally the moe_prepare_mxfp4_scales output of these scales (uint8, 16-byte aligned)."""
-    w1: torch.Tensor
+    optionally the moe_prepare_mxfp4_scales output of these scales and the moe_prepare_mxfp4_weights
+    output of these weights (uint8, 16-byte aligned; with it, w1/w3/w2 may be None)."""
+    w1: torch.Tensor | None
     s1: torch.Tensor
-    w3: torch.Tensor
+    w3: torch.Tensor | None
     s3: torch.Tensor
-    w2: torch.Tensor
+    w2: torch.Tensor | None
     s2: torch.Tensor
     stage_scales: torch.Tensor | None = None
+    tiled_weights: torch.Tensor | None = None
 
     def c(self) -> _MXFP4:
-        return _MXFP4(*(_ptr(getattr(self, n), torch.uint8) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")))
+        return _MXFP4(*(_ptr(getattr(self, n), torch.uint8)
+                        for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales", "tiled_weights")))
 
 
 @dataclass
@@ -344,6 +352,23 @@ def moe_prepare_mxfp4_scales(dims: Dims, packed: MXFP4Experts, out=None, stream=
     st = lib.moe_prepare_mxfp4_scales(ctypes.byref(dims.c()), ctypes.byref(packed.c()), _ptr(out, torch.uint8),
                                       _stream(stream))
     _check(st, "moe_prepare_mxfp4_scales")
+    return out
+
+
+def moe_mxfp4_tiled_weights_bytes(dims: Dims) -> int:
+    return int(lib.moe_mxfp4_tiled_weights_bytes(ctypes.byref(dims.c())))
+
+
+def moe_prepare_mxfp4_weights(dims: Dims, packed: MXFP4Experts, out=None, stream=None) -> torch.Tensor:
+    """The fragment-order copy of packed's w1, w3, w2 (into out, or a new uint8 tensor on their device)."""
+    n = moe_mxfp4_tiled_weights_bytes(dims)
+    if n == 0:
+        raise MoeError("invalid dims for tiled weights")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=packed.w1.device)
+    st = lib.moe_prepare_mxfp4_weights(ctypes.byref(dims.c()), ctypes.byref(packed.c()), _ptr(out, torch.uint8),
+                                       _stream(stream))
+    _check(st, "moe_prepare_mxfp4_weights")
     return out
 
 

@@ -238,6 +238,9 @@ namespace {
 
 constexpr int kStreamU = 4;   // K steps of weight loads in flight per lane
 constexpr int kStreamRows = 4;   // activation rows staged in LDS per pass
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for
+// vmcnt(0) lgkmcnt(0), expcnt left at its maximum (not waited for)
+constexpr int kWaitVmLgkm0 = 0x7 << 4;
 
 // Direct global -> LDS copy of a run of nbytes (a multiple of UNIT = 16 or 4) by one wave: lane i moves
 // UNIT bytes of every 64 * UNIT-byte piece (the copy lands at lds + off + i * UNIT). Every copy of the
@@ -256,11 +259,16 @@ __device__ __forceinline__ void stage_run(uint8_t* lds, const uint8_t* src, int 
 
 template <int WF>
 struct StreamA;   // one 16-row x 128-K weight fragment of a lane
+// `src` is the lane's first 16 bytes and KSTRIDE the bytes between consecutive 128-wide K steps: 64
+// along a stored row, 1024 between the fragments of the fragment-order copy. (A compile-time stride
+// keeps the prefetch addresses immediate offsets; computed at run time, the compiler waited for every
+// load in flight before issuing the next.)
 template <>
 struct StreamA<W_MXFP4> {
   u32x4 d;
-  __device__ __forceinline__ void load(const uint8_t* row, int ks, int g) {
-    d = *reinterpret_cast<const u32x4*>(row + ks * 64 + 16 * g);
+  template <int KSTRIDE>
+  __device__ __forceinline__ void load(const uint8_t* src, int ks) {
+    d = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE);
   }
   __device__ __forceinline__ i32x8 frag() const {
     return i32x8{(int)d[0], (int)d[1], (int)d[2], (int)d[3], 0, 0, 0, 0};
@@ -270,9 +278,10 @@ struct StreamA<W_MXFP4> {
 template <>
 struct StreamA<W_FP8_BLOCK32> {
   u32x4 d0, d1;
-  __device__ __forceinline__ void load(const uint8_t* row, int ks, int g) {
-    d0 = *reinterpret_cast<const u32x4*>(row + ks * 128 + 16 * g);
-    d1 = *reinterpret_cast<const u32x4*>(row + ks * 128 + 64 + 16 * g);
+  template <int KSTRIDE>
+  __device__ __forceinline__ void load(const uint8_t* src, int ks) {
+    d0 = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE);
+    d1 = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE + 64);
   }
   __device__ __forceinline__ i32x8 frag() const {
     return i32x8{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
@@ -284,8 +293,9 @@ struct StreamA<W_FP8_BLOCK32> {
 
 // Dynamic LDS: scales [64][K/32], activation codes [4][K], activation scales [4][K/32], then the
 // [4 waves][64 lanes] fp32x4 exchange of the fragments.
-template <int WF, bool GEMM1>
+template <int WF, bool GEMM1, bool TILED>
 __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
+  static_assert(!TILED || WF == W_MXFP4, "the fragment-order copy holds MXFP4 codes");
   extern __shared__ __align__(16) uint8_t dyn[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -309,8 +319,12 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   auto grow_of = [&](int r) { return GEMM1 ? c0 + (r & 31) : c0 + r; };
   const size_t wrow_bytes = (WF == W_MXFP4) ? (size_t)K / 2 : (size_t)K;
   const int lrow = (GEMM1 ? 32 * (wave >> 1) + 16 * (wave & 1) : 16 * wave) + r16;   // this wave's fragment
-  const uint8_t* wrow = static_cast<const uint8_t*>((GEMM1 && wave >= 2) ? p.wb : p.wa) +
-                        (size_t)e * p.w_expert_stride + (size_t)grow_of(lrow) * wrow_bytes;
+  // the lane's weight bytes of K step 0 and the stride between steps: along its stored row (16 bytes of
+  // K block g), or, in the fragment-order copy, lane's 16 bytes of fragment (row / 16, step)
+  const uint8_t* wmat = static_cast<const uint8_t*>((GEMM1 && wave >= 2) ? p.wb : p.wa) + (size_t)e * p.w_expert_stride;
+  constexpr int kKStride = TILED ? 1024 : (WF == W_MXFP4 ? 64 : 128);
+  const uint8_t* wsrc = TILED ? wmat + ((size_t)(grow_of(lrow) >> 4) * nk) * 1024 + 16 * lane
+                              : wmat + (size_t)grow_of(lrow) * wrow_bytes + 16 * g;
 
   for (int tg = 0; tg < nrows; tg += kStreamRows) {
     const int n = min(kStreamRows, nrows - tg);
@@ -344,18 +358,20 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
       }
     }
     // the first weight batch (in bounds for any nk: short K repeats the last step)
-    StreamA<WF> A[kStreamU];
+    // two register sets in turn (no copies between them): while the MFMAs run on one set's kStreamU steps,
+    // the other set's loads are in flight.
+    StreamA<WF> A[kStreamU], Bs[kStreamU];
 #pragma unroll
-    for (int u = 0; u < kStreamU; ++u) A[u].load(wrow, min(u, nk - 1), g);
-    // every copy of this wave has landed in LDS (vmcnt counts the LDS-bound loads too); then meet
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int u = 0; u < kStreamU; ++u) A[u].template load<kKStride>(wsrc, min(u, nk - 1));
+    // every copy of this wave has landed in LDS (vmcnt counts the LDS-bound loads too); then meet. The
+    // wait is the builtin, not inline asm, so that the compiler knows the copies are done: otherwise it
+    // counts them as outstanding, and with loads of two kinds in flight it waits for all of them (vmcnt(0))
+    // before every use of a weight register, leaving only one batch of steps in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    __builtin_amdgcn_s_barrier();
     const int bt = r16 & (kStreamRows - 1);   // lanes past the staged rows compute a staged row (discarded)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int ks0 = 0; ks0 < nk; ks0 += kStreamU) {
-      StreamA<WF> An[kStreamU];
-#pragma unroll
-      for (int u = 0; u < kStreamU; ++u)
-        if (ks0 + kStreamU + u < nk) An[u].load(wrow, ks0 + kStreamU + u, g);
+    auto run = [&](const StreamA<WF> (&R)[kStreamU], int ks0) {
 #pragma unroll
       for (int u = 0; u < kStreamU; ++u) {
         const int ks = ks0 + u;
@@ -364,13 +380,36 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
           const u32x4 b1 = *reinterpret_cast<const u32x4*>(xb + bt * K + ks * 128 + 64 + 16 * g);
           const i32x8 B = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2],
                                 (int)b1[3]};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[u].frag(), B, acc, StreamA<WF>::kFmt, 0, 0,
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(R[u].frag(), B, acc, StreamA<WF>::kFmt, 0, 0,
                                                                  (int)sc[(WF == W_MXFP4 ? lrow : lrow >> 5) * KB + 4 * ks + g], 0,
                                                                  (int)xsb[bt * KB + 4 * ks + g]);
         }
       }
+    };
+    // The loads are never conditional: with a guarded load the compiler no longer knows how many loads
+    // are in flight and waits for all of them before each MFMA. Steps past the last re-read it (in
+    // bounds, unused). Measured choice: on the fragment-order copy every batch is issued, also the one
+    // after the last step; on the stored layout (GEMM2: 18 steps) the loop leaves before a batch that
+    // has no step.
+    for (int ks0 = 0; ks0 < nk; ks0 += 2 * kStreamU) {
+      if constexpr (!TILED) {
+        if (ks0 + kStreamU >= nk) {
+          run(A, ks0);
+          break;
+        }
+      }
 #pragma unroll
-      for (int u = 0; u < kStreamU; ++u) A[u] = An[u];
+      for (int u = 0; u < kStreamU; ++u) Bs[u].template load<kKStride>(wsrc, min(ks0 + kStreamU + u, nk - 1));
+      run(A, ks0);
+      if constexpr (!TILED) {
+        if (ks0 + 2 * kStreamU >= nk) {
+          run(Bs, ks0 + kStreamU);
+          break;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) A[u].template load<kKStride>(wsrc, min(ks0 + 2 * kStreamU + u, nk - 1));
+      run(Bs, ks0 + kStreamU);
     }
     // the four fragments meet in LDS; wave 0 runs the epilogue (lane: weight rows 4g..4g+3, row r16)
     xch[wave * 64 + lane] = acc;
@@ -439,8 +478,11 @@ static void launch_stream(WeightFormat f, const GemmProblem& p, int max_active, 
   dim3 grid(GEMM1 ? p.N / 32 : p.N / 64, p.dense ? 1 : max_active);
   const size_t lds = stream_lds_bytes(p.K);
   switch (f) {
-    case W_MXFP4: expert_gemm_stream<W_MXFP4, GEMM1><<<grid, dim3(256), lds, s>>>(p); break;
-    case W_FP8_BLOCK32: expert_gemm_stream<W_FP8_BLOCK32, GEMM1><<<grid, dim3(256), lds, s>>>(p); break;
+    case W_MXFP4:
+      if (p.w_tiled) expert_gemm_stream<W_MXFP4, GEMM1, true><<<grid, dim3(256), lds, s>>>(p);
+      else expert_gemm_stream<W_MXFP4, GEMM1, false><<<grid, dim3(256), lds, s>>>(p);
+      break;
+    case W_FP8_BLOCK32: expert_gemm_stream<W_FP8_BLOCK32, GEMM1, false><<<grid, dim3(256), lds, s>>>(p); break;
     default: break;   // the bf16 arm uses launch_small
   }
 }

@@ -151,10 +151,11 @@ constexpr int loads_per_stage() { return (WF == W_MXFP4 ? 4 : 8) + 16 / (TN / 64
 // w so that every XCD gets one contiguous range of the work list, and the list runs expert by expert,
 // column tile by column tile, row tile by row tile: the blocks an XCD runs together share a weight tile
 // and the expert's activation rows stay in that XCD's L2.
-template <int WF, bool GEMM1, int TN>
+template <int WF, bool GEMM1, int TN, bool TILED>
 __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const int32_t* __restrict__ tile_e,
                                                            const int32_t* __restrict__ tile_r0,
                                                            const int32_t* __restrict__ info) {
+  static_assert(!TILED || WF == W_MXFP4, "the fragment-order copy holds MXFP4 codes");
   using T = WTraits<WF>;
   constexpr int kRB = T::kRowBytes, kCh = kRB / 16;
   constexpr int NW = TN / 64;                          // waves (each 128 weight rows x 64 activation rows)
@@ -205,13 +206,19 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
   auto grow_of = [&](int r) { return GEMM1 ? n0 + (r % (TN / 2)) : min(n0 + r, p.N - 1); };
 
   // ---- per-lane DMA sources (the stage offset is added per stage) ------------------------------
+  // An MXFP4 instruction moves one 16-row fragment (16 rows x 64 B). In the fragment-order copy those
+  // 1024 bytes are contiguous (lane l' = 16 c + row % 16 holds logical chunk c of the row), so the lanes
+  // of one copy read one contiguous kilobyte, in the permuted order the LDS swizzle asks for.
+  constexpr int wstage = TILED ? 1024 : (WF == W_MXFP4 ? kStepK / 2 : kStepK);   // bytes between stages
   const uint8_t* wsrc[kWInstr];
 #pragma unroll
   for (int i = 0; i < kWInstr; ++i) {
     const int r = wave * 64 + i * kWRows + lane / kCh;             // LDS weight row
     const int gc = (lane % kCh) ^ chunk_key<kRB>(r);               // physical chunk lane%kCh holds logical gc
-    const uint8_t* base = static_cast<const uint8_t*>((GEMM1 && r >= TN / 2) ? p.wb : p.wa);
-    wsrc[i] = base + (size_t)e * p.w_expert_stride + (size_t)grow_of(r) * wrow_bytes + gc * 16;
+    const uint8_t* base = static_cast<const uint8_t*>((GEMM1 && r >= TN / 2) ? p.wb : p.wa) + (size_t)e * p.w_expert_stride;
+    const int gr = grow_of(r);
+    wsrc[i] = TILED ? base + ((size_t)(gr >> 4) * nk) * 1024 + (16 * gc + (gr & 15)) * 16
+                    : base + (size_t)gr * wrow_bytes + gc * 16;
   }
   auto act_row = [&](int t) {   // activation row of LDS row t (rows past the tile repeat row 0)
     const int pos = row0 + (t < nrows ? t : 0);
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     const int k0 = s * kStepK;
 #pragma unroll
     for (int i = 0; i < kWInstr; ++i)
-      dma16(wsrc[i] + (WF == W_MXFP4 ? k0 / 2 : k0), &st.w[(wave * 64 + i * kWRows) * kRB]);
+      dma16(wsrc[i] + s * wstage, &st.w[(wave * 64 + i * kWRows) * kRB]);
 #pragma unroll
     for (int i = 0; i < kAInstr; ++i) dma16(asrc[i] + k0, &st.a[(wave * kARows + i * 8) * kStepK]);
     dma4(wssrc + (size_t)s * ws_step, &st.ws[wave * 64 * 4]);
@@ -460,7 +467,7 @@ struct DaStage {
 
 }  // namespace
 
-template <bool GEMM1>
+template <bool GEMM1, bool TILED>
 __global__ __launch_bounds__(256, 2) void expert_gemm_mfma_da(GemmProblem p, const int32_t* __restrict__ tile_e,
                                                               const int32_t* __restrict__ tile_r0,
                                                               const int32_t* __restrict__ info) {
@@ -492,9 +499,14 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_mfma_da(GemmProblem p, con
   // matrix is N * K / 2 < 2^31 bytes)
   const uint8_t* wbase_a = static_cast<const uint8_t*>(p.wa) + (size_t)e * p.w_expert_stride;
   const uint8_t* wbase_b = GEMM1 ? static_cast<const uint8_t*>(p.wb) + (size_t)e * p.w_expert_stride : wbase_a;
+  // (fragment-order copy: lane's 16 bytes of fragment (row / 16, step), 1024 bytes between steps;
+  // rows past N repeat the last fragment, whose outputs are never stored)
   uint32_t aoff[4];
+  constexpr int astage = TILED ? 1024 : kStepK / 2;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) aoff[a] = (uint32_t)grow(a, r16) * (uint32_t)(K / 2) + 16u * g;
+  for (int a = 0; a < 4; ++a)
+    aoff[a] = TILED ? (uint32_t)(min(grow(a, 0), p.N - 16) >> 4) * (uint32_t)nk * 1024u + 16u * lane
+                    : (uint32_t)grow(a, r16) * (uint32_t)(K / 2) + 16u * g;
   // per-stage copies: activation rows (4 of 8 rows x 128 B per wave), weight scales (the wave's 64 rows,
   // 4 bytes each), activation scales (32 rows per wave, 4 bytes each)
   auto act_row = [&](int t) {
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_mfma_da(GemmProblem p, con
   auto load_a = [&](u32x4 (&A)[4], int s) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      A[a] = *reinterpret_cast<const u32x4*>(((GEMM1 && a >= 2) ? wbase_b : wbase_a) + aoff[a] + s * (kStepK / 2));
+      A[a] = *reinterpret_cast<const u32x4*>(((GEMM1 && a >= 2) ? wbase_b : wbase_a) + aoff[a] + s * astage);
   };
 
   // B fragments of this wave's 128 rows that hold a row of the tile (the last tile of an expert is partial)
@@ -602,8 +614,7 @@ __global__ __launch_bounds__(256, 2) void expert_gemm_mfma_da(GemmProblem p, con
 #pragma unroll
       for (int a = 0; a < 4; ++a) A0[a] = A1[a];
     }
-  };
-  if (nbv == 8) kloop(kFull);
+  };  if (nbv == 8) kloop(kFull);
   else kloop(kPartial);
 
   // ---- epilogue: lane holds weight rows 4g..4g+3 of each A fragment for activation row r16 of each B
@@ -713,7 +724,13 @@ static void launch_mfma_tn(const GemmProblem& p, int max_tiles, const int32_t* t
                            const int32_t* info, hipStream_t s) {
   const int cols = GEMM1 ? p.N / (TN / 2) : (p.N + TN - 1) / TN;
   const int rows = p.dense ? (p.M + kTileM - 1) / kTileM : max_tiles;
-  expert_gemm_mfma<WF, GEMM1, TN><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
+  if constexpr (WF == W_MXFP4) {
+    if (p.w_tiled) {
+      expert_gemm_mfma<WF, GEMM1, TN, true><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
+      return;
+    }
+  }
+  expert_gemm_mfma<WF, GEMM1, TN, false><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
 }
 
 // MXFP4 weights: 512 weight rows per block (8 waves) when the columns divide evenly, else 256; FP8 weights
@@ -727,8 +744,9 @@ static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, con
         if (p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 512>(p, max_tiles, tile_e, tile_r0, info, s);
         else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
       } else {   // short K: weights straight into registers, two blocks per CU overlap their epilogues
-        expert_gemm_mfma_da<false><<<dim3(((p.N + 255) / 256) * max_tiles), dim3(256), 0, s>>>(p, tile_e, tile_r0,
-                                                                                               info);
+        const dim3 grid(((p.N + 255) / 256) * max_tiles);
+        if (p.w_tiled) expert_gemm_mfma_da<false, true><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0, info);
+        else expert_gemm_mfma_da<false, false><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0, info);
       }
       break;
     case W_FP8_BLOCK32: launch_mfma_tn<W_FP8_BLOCK32, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s); break;

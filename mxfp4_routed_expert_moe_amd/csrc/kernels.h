@@ -69,6 +69,9 @@ struct GemmProblem {
   int a_stage_major;
   // GEMM1 output scales h_s written stage-major, [N/128][M*k][4], for a GEMM2 with a_stage_major
   int h_s_stage_major;
+  // MXFP4 weight codes in fragment order (launch_tile_mxfp4): per expert [N/16][K/128][64 lanes][16 B]
+  // instead of [N][K/2]; same expert stride
+  int w_tiled;
 };
 // GEMM1: g = w1 x, u = w3 x -> bf16 -> SwiGLU (x rw) -> bf16 -> QDQ per 32 -> h_q, h_s
 void launch_gemm1_small(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
@@ -128,6 +131,9 @@ void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slo
                     const uint16_t* shared_out, uint16_t* out, hipStream_t s);
 
 // ---- expansion of packed experts to bf16 (expand.hip) --------------------------------------
+// Fragment order of packed E2M1 codes: mats matrices w[m][N][K/2] -> T[m][N/16][K/128][64][16] with
+// T[m][f][q][l][b] = w[m][16 f + l % 16][64 q + 16 (l / 16) + b] (N % 16 == 0, K % 128 == 0).
+void launch_tile_mxfp4(int mats, int N, int K, const uint8_t* w, uint8_t* out, hipStream_t s);
 void launch_expand_mxfp4(long long rows, int cols, const uint8_t* w, const uint8_t* sc, uint16_t* out,
                          hipStream_t s);
 

@@ -96,11 +96,22 @@ moe_status launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ER
     if (st_ != MOE_OK) return st_;      \
   } while (0)
 
+// The weight codes come from w1, w3, w2 or, when given, from the fragment-order copy (then the three
+// row-major pointers may be NULL); the scales always from s1, s3, s2.
 moe_status check_packed(const moe_mxfp4_experts* w) {
-  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16))
+  if (!w || !al(w->s1, 16) || !al(w->s3, 16) || !al(w->s2, 16)) return MOE_ERR_INVALID_ARG;
+  if (w->tiled_weights != nullptr) {
+    if (!al(w->tiled_weights, 16)) return MOE_ERR_INVALID_ARG;
+  } else if (!al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16)) {
     return MOE_ERR_INVALID_ARG;
+  }
   if (w->stage_scales != nullptr && !al(w->stage_scales, 16)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// Offset of w1, w3, w2 inside moe_prepare_mxfp4_weights output (each matrix stack is E * I * H / 2 bytes).
+inline size_t tiled_off(const moe_dims* d, int which) {
+  return (size_t)which * d->num_experts * (size_t)d->inter * (d->hidden / 2);
 }
 
 // Offsets of the s1, s3, s2 stage-major copies inside moe_prepare_mxfp4_scales output (and the
@@ -178,6 +189,11 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
     f = moe::W_MXFP4;
     p.wa = packed->w1; p.sa = packed->s1; p.wb = packed->w3; p.sb = packed->s3;
     p.w_expert_stride = (long long)I * H / 2; p.s_expert_stride = (long long)I * H / 32;
+    if (packed->tiled_weights != nullptr) {
+      p.wa = packed->tiled_weights + tiled_off(d, 0);
+      p.wb = packed->tiled_weights + tiled_off(d, 1);
+      p.w_tiled = 1;
+    }
   } else {
     f = moe::W_BF16;
     p.wa = decoded->w1; p.sa = nullptr; p.wb = decoded->w3; p.sb = nullptr;
@@ -222,6 +238,10 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
     f = moe::W_MXFP4;
     q.wa = packed->w2; q.sa = packed->s2;
     q.w_expert_stride = (long long)H * I / 2; q.s_expert_stride = (long long)H * I / 32;
+    if (packed->tiled_weights != nullptr) {
+      q.wa = packed->tiled_weights + tiled_off(d, 2);
+      q.w_tiled = 1;
+    }
   } else {
     f = moe::W_BF16;
     q.wa = decoded->w2; q.sa = nullptr;
@@ -596,6 +616,28 @@ moe_status moe_prepare_mxfp4_scales(const moe_dims* dims, const moe_mxfp4_expert
   moe::launch_scales_stage_major(E, I, H, w->s1, out + stage_scales_off(dims, 0), s);
   moe::launch_scales_stage_major(E, I, H, w->s3, out + stage_scales_off(dims, 1), s);
   moe::launch_scales_stage_major(E, H, I, w->s2, out + stage_scales_off(dims, 2), s);
+  return launched();
+}
+
+size_t moe_mxfp4_tiled_weights_bytes(const moe_dims* dims) {
+  if (check_dims(dims, 0) != MOE_OK) return 0;
+  return tiled_off(dims, 3);
+}
+
+moe_status moe_prepare_mxfp4_weights(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream) {
+  MOE_TRY(check_dims(dims, 0));
+  if (!w || !al(w->w1, 16) || !al(w->w3, 16) || !al(w->w2, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t n = tiled_off(dims, 3), per = tiled_off(dims, 1);
+  auto overlaps = [&](const uint8_t* a) {
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out), p = reinterpret_cast<uintptr_t>(a);
+    return p < o + n && o < p + per;
+  };
+  if (overlaps(w->w1) || overlaps(w->w3) || overlaps(w->w2)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = dims->num_experts, H = dims->hidden, I = dims->inter;
+  moe::launch_tile_mxfp4(E, I, H, w->w1, out + tiled_off(dims, 0), s);
+  moe::launch_tile_mxfp4(E, I, H, w->w3, out + tiled_off(dims, 1), s);
+  moe::launch_tile_mxfp4(E, H, I, w->w2, out + tiled_off(dims, 2), s);
   return launched();
 }
 

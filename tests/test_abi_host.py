@@ -40,7 +40,7 @@ class Six(ctypes.Structure):
 
 
 class Packed(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "s1", "w3", "s3", "w2", "s2", "stage_scales", "tiled_weights")]
 
 
 class Three(ctypes.Structure):
@@ -123,6 +123,9 @@ def test_forward_refuses_before_launch(lib):
     assert _forward(lib, d, 8, shared_out=FAKE) == INVALID               # shared_out without a shared expert
     assert _forward(lib, d, 8, packed=Packed(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, None)) == INVALID   # misaligned scales
     assert _forward(lib, d, 8, packed=Packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8)) == INVALID   # misaligned copy
+    assert _forward(lib, d, 8, packed=Packed(0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)) == INVALID    # no w1 codes
+    assert _forward(lib, d, 8, packed=Packed(0, FAKE, 0, FAKE, 0, FAKE, None, FAKE + 8)) == INVALID      # misaligned tiles
+    assert _forward(lib, d, 8, packed=Packed(0, 0, 0, FAKE, 0, FAKE, None, FAKE)) == INVALID             # tiles, no s1
     assert _forward(lib, d, 8, shared=Six(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8)) == INVALID  # misaligned scales
     assert _forward(lib, Dims(128, 5120, 2304, 9, 1.5), 8) == UNSUPPORTED
     assert _forward(lib, Dims(512, 5120, 2304, 6, 1.5), 8) == UNSUPPORTED
@@ -179,3 +182,24 @@ def test_stage_scales_size_and_refusals(lib):
     assert prep(ctypes.byref(big()), ctypes.byref(ok), FAKE + 4, None) == INVALID
     assert prep(ctypes.byref(big()), ctypes.byref(Packed(FAKE, 0, FAKE, FAKE, FAKE, FAKE, None)), FAKE, None) == INVALID
     assert prep(ctypes.byref(Dims(128, 5056, 2304, 6, 1.5)), ctypes.byref(ok), FAKE, None) == UNSUPPORTED
+
+
+def test_prepare_tiled_weights_refuses_before_launch(lib):
+    size = lib.moe_mxfp4_tiled_weights_bytes
+    size.argtypes = [ctypes.POINTER(Dims)]
+    size.restype = ctypes.c_size_t
+    d = big()
+    assert size(ctypes.byref(d)) == 3 * 128 * 2304 * 5120 // 2     # the three code matrices, same bytes
+    assert size(ctypes.byref(Dims(128, 5000, 2304, 6, 1.5))) == 0
+    f = lib.moe_prepare_mxfp4_weights
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    w1, w3, w2 = FAKE, FAKE + (1 << 32), FAKE + (2 << 32)
+    ok = Packed(w1, FAKE, w3, FAKE, w2, FAKE, None, None)
+    assert f(ctypes.byref(d), ctypes.byref(ok), ctypes.c_void_p(FAKE + 8), None) == INVALID    # misaligned out
+    assert f(ctypes.byref(d), ctypes.byref(ok), ctypes.c_void_p(w3 + 4096), None) == INVALID   # overlaps w3
+    assert f(ctypes.byref(d), None, ctypes.c_void_p(FAKE + (3 << 32)), None) == INVALID
+    assert f(ctypes.byref(d), ctypes.byref(Packed(w1, FAKE, 0, FAKE, w2, FAKE, None, None)),
+             ctypes.c_void_p(FAKE + (3 << 32)), None) == INVALID                               # no w3
+    assert f(ctypes.byref(Dims(128, 5120, 2300, 6, 1.5)), ctypes.byref(ok), ctypes.c_void_p(FAKE + (3 << 32)),
+             None) == UNSUPPORTED

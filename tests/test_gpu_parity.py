@@ -532,3 +532,59 @@ def test_forward_with_prepared_scales_is_identical(over):
     m().moe_forward(dims, d["x"], d["gate_w"], d["gate_b"], pk, None, None, out, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), a["out_bits"])
+
+
+def test_prepare_mxfp4_weights_layout():
+    """moe_prepare_mxfp4_weights stores w1, w3, w2 in fragment order [E, N/16, K/128, 64, 16], lane l of
+    fragment (f, q) holding row 16 f + l % 16, bytes 64 q + 16 (l / 16) .. + 15 (checked against a host
+    permutation of the weight tensors)."""
+    cfg, inp, d = cfg_inputs(0, M=8, H=512, I=384, E=8, k=2)
+    out = m().moe_prepare_mxfp4_weights(dims_of(cfg), packed_of(d))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    parts = []
+    for name, N, K in (("w1", cfg.I, cfg.H), ("w3", cfg.I, cfg.H), ("w2", cfg.H, cfg.I)):
+        w = inp[name].reshape(cfg.E, N // 16, 16, K // 128, 4, 16)   # e, f, row in fragment, q, g, byte
+        parts.append(np.ascontiguousarray(w.transpose(0, 1, 3, 4, 2, 5)).ravel())
+    assert got.size == m().moe_mxfp4_tiled_weights_bytes(dims_of(cfg))
+    assert np.array_equal(got, np.concatenate(parts))
+
+
+TILED_CASES = [dict(M=1000, H=512, I=256, E=8, k=2), dict(M=1000, H=512, I=384, E=8, k=2),
+               dict(M=37, H=512, I=256, E=8, k=2)]
+
+
+@pytest.mark.parametrize("over", TILED_CASES, ids=["prefill_width", "prefill_width_I384", "decode_width"])
+def test_forward_with_tiled_weights_is_identical(over):
+    """With the fragment-order copy of the weights (and no row-major weight pointers at all) every GEMM
+    reads the same codes from other addresses: outputs equal the call on the stored layout bit for bit,
+    at prefill width (both GEMM1 tile widths) and at decode width."""
+    cfg, inp, d = cfg_inputs(0, **over)
+    a = forward(cfg, d)
+    pk = packed_of(d)
+    tiled = m().moe_prepare_mxfp4_weights(dims_of(cfg), pk)
+    pk = m().MXFP4Experts(None, d["s1"], None, d["s3"], None, d["s2"], tiled_weights=tiled)
+    dims = dims_of(cfg)
+    ws = m().workspace(dims, cfg.M)
+    out = torch.empty((cfg.M, cfg.H), dtype=torch.int16, device="cuda")
+    m().moe_forward(dims, d["x"], d["gate_w"], d["gate_b"], pk, None, None, out, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a["out_bits"])
+
+
+@pytest.mark.parametrize("M", [8, 8192])
+def test_full_size_layer_with_tiled_weights_is_identical(M):
+    """The full-size layer (hidden 5120, 128 experts, intermediate 2304, top-6) with the fragment-order
+    weights and prepared scales, at decode and prefill width, equals the call on the stored layout."""
+    cfg, inp, d = cfg_inputs(3)
+    c = synth.get_config(3, M=M)
+    a = forward(c, d, M=M)
+    pk = packed_of(d)
+    pk.stage_scales = m().moe_prepare_mxfp4_scales(dims_of(c), pk)
+    pk.tiled_weights = m().moe_prepare_mxfp4_weights(dims_of(c), pk)
+    dims = dims_of(c)
+    ws = m().workspace(dims, M)
+    out = torch.empty((M, c.H), dtype=torch.int16, device="cuda")
+    m().moe_forward(dims, d["x"][:M], d["gate_w"], d["gate_b"], pk, None, None, out, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a["out_bits"])
