@@ -31,7 +31,6 @@ namespace {
 
 constexpr int kTileM = 128;   // activation rows per block (weight rows per block: the TN template argument)
 constexpr int kStepK = 128;   // K per stage (one MFMA K)
-constexpr int kStages = 3;    // LDS ring depth: stage s + 2 is in flight while stage s is computed
 constexpr int kFmtFp8 = 0, kFmtFp4 = 4;   // operand formats of the scaled MFMA
 
 template <int WF>
@@ -151,8 +150,11 @@ constexpr int loads_per_stage() { return (WF == W_MXFP4 ? 4 : 8) + 16 / (TN / 64
 // w so that every XCD gets one contiguous range of the work list, and the list runs expert by expert,
 // column tile by column tile, row tile by row tile: the blocks an XCD runs together share a weight tile
 // and the expert's activation rows stay in that XCD's L2.
-template <int WF, bool GEMM1, int TN, bool TILED>
-__global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const int32_t* __restrict__ tile_e,
+// PAIR: 4 waves and a two-stage ring (67 KB of LDS), two blocks per CU; their waves share the SIMDs, and
+// because the two blocks meet at their own barriers, one block's fragment reads and copies overlap the
+// other's MFMAs. Otherwise one block per CU with a three-stage ring.
+template <int WF, bool GEMM1, int TN, bool TILED, bool PAIR = false>
+__global__ __launch_bounds__(TN, PAIR ? 2 : 1) void expert_gemm_mfma(GemmProblem p, const int32_t* __restrict__ tile_e,
                                                            const int32_t* __restrict__ tile_r0,
                                                            const int32_t* __restrict__ info) {
   static_assert(!TILED || WF == W_MXFP4, "the fragment-order copy holds MXFP4 codes");
@@ -164,6 +166,8 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
   constexpr int kAInstr = 16 / NW;                     // activation DMA per wave per stage
   constexpr int kARows = kTileM / NW;                  // activation rows per wave
   constexpr int LPS = loads_per_stage<WF, TN>();
+  constexpr int kStages = PAIR ? 2 : 3;   // LDS ring depth
+  static_assert(!PAIR || TN == 256, "two blocks per CU: 4 waves");
   __shared__ __align__(16) Stage<WF, TN> ring[kStages];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     }
   };
 
-  if constexpr (NW == 4) {
+  if constexpr (NW == 4 && !PAIR) {
     // one wave per SIMD: fragments double-buffered in registers, LDS reads of stage s + 1 interleaved
     // with the MFMAs of stage s
     Frags<WF> F0, F1;
@@ -365,14 +369,16 @@ __global__ __launch_bounds__(TN, 1) void expert_gemm_mfma(GemmProblem p, const i
     // two waves per SIMD cover each other's LDS latency: one fragment set (fits 256 registers)
     // (a partial tile, the last one of an expert, runs its own copy of the loop that skips the empty
     // B fragments; full tiles run a copy without the checks)
+    // (two-stage ring: stage s + 1 is issued at step s, so each wait is for everything in flight)
     Frags<WF> F;
+    constexpr int D = kStages - 1;   // stages in flight ahead of the one computed
     issue(0);
-    if (nk > 1) issue(1);
+    if (D > 1 && nk > 1) issue(1);
     auto kloop = [&](auto part) {
       for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk) ring_barrier<LPS>();   // stage s landed (stage s + 1 may still be in flight)
+        if (D > 1 && s + 1 < nk) ring_barrier<LPS>();   // stage s landed (stage s + 1 may still be in flight)
         else ring_barrier<0>();
-        if (s + 2 < nk) issue(s + 2);           // into the slot computed at s - 1: every wave is past it
+        if (s + D < nk) issue(s + D);           // into the slot computed at s - 1: every wave is past it
         read_frags(F, s, part);
         mfmas(F, part);
       }
@@ -719,18 +725,18 @@ void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile
   tile_map_kernel<<<dim3(1), dim3(256), 0, s>>>(E, max_tiles, offsets, tile_e, tile_r0, info);
 }
 
-template <int WF, bool GEMM1, int TN>
+template <int WF, bool GEMM1, int TN, bool PAIR = false>
 static void launch_mfma_tn(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
                            const int32_t* info, hipStream_t s) {
   const int cols = GEMM1 ? p.N / (TN / 2) : (p.N + TN - 1) / TN;
   const int rows = p.dense ? (p.M + kTileM - 1) / kTileM : max_tiles;
   if constexpr (WF == W_MXFP4) {
     if (p.w_tiled) {
-      expert_gemm_mfma<WF, GEMM1, TN, true><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
+      expert_gemm_mfma<WF, GEMM1, TN, true, PAIR><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
       return;
     }
   }
-  expert_gemm_mfma<WF, GEMM1, TN, false><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
+  expert_gemm_mfma<WF, GEMM1, TN, false, PAIR><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
 }
 
 // MXFP4 weights: 512 weight rows per block (8 waves) when the columns divide evenly, else 256; FP8 weights
@@ -741,7 +747,7 @@ static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, con
   switch (f) {
     case W_MXFP4:
       if constexpr (GEMM1) {   // long K: the 512-row LDS ring streams best
-        if (p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 512>(p, max_tiles, tile_e, tile_r0, info, s);
+        if (p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
         else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
       } else {   // short K: weights straight into registers, two blocks per CU overlap their epilogues
         const dim3 grid(((p.N + 255) / 256) * max_tiles);
