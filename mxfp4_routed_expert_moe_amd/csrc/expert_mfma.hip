@@ -16,8 +16,10 @@
 // Tiling. A block computes 256 weight rows x 128 rows of one expert (GEMM1: the same 128 output columns
 // of w1 and w3, so the SwiGLU pairs sit in one lane). Four waves in a 2 x 2 layout each own 128 weight
 // rows x 64 rows (32 MFMAs per 128-wide K step, 128 fp32 accumulators per lane: the larger wave tile
-// cuts LDS bytes per MFMA). K steps of 128 stream into a three-stage LDS ring by direct global-to-LDS
-// copies issued two stages ahead, with XOR-swizzled 16-byte chunks (conflict-free fragment reads). The rows of
+// cuts LDS bytes per MFMA). K steps of 128 stream into an LDS ring by direct global-to-LDS copies, with
+// XOR-swizzled 16-byte chunks (conflict-free fragment reads): for MXFP4 weights a two-stage ring and two
+// blocks per CU, whose waves share the SIMDs and overlap each other's copies, fragment reads and MFMAs;
+// for FP8 weights a three-stage ring issued two stages ahead, one block per CU. The rows of
 // an expert are its sorted positions offsets[e] .. offsets[e+1]; GEMM1 gathers the activation row of
 // each position's token, GEMM2 reads the QDQ'd h rows in sorted order and scatters y to the pair's slot
 // row. The (expert, row tile) of a block comes from a tile list built on the device from the expert
@@ -739,20 +741,22 @@ static void launch_mfma_tn(const GemmProblem& p, int max_tiles, const int32_t* t
   expert_gemm_mfma<WF, GEMM1, TN, false, PAIR><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
 }
 
-// MXFP4 weights: 512 weight rows per block (8 waves) when the columns divide evenly, else 256; FP8 weights
-// (twice the bytes per row): 256.
+// MXFP4 weights, GEMM1: 256 weight rows per block, two blocks per CU (measured at M = 8192: 1.20 ms, against
+// 1.29 ms for 512-row blocks of 8 waves with a three-stage ring, one block per CU). GEMM2: see below. FP8
+// weights (twice the bytes per row): 256 rows, one block per CU.
 template <bool GEMM1>
 static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
                         const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
   switch (f) {
     case W_MXFP4:
-      if constexpr (GEMM1) {   // long K: the 512-row LDS ring streams best
-        if (p.N % 256 == 0) launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
-        else launch_mfma_tn<W_MXFP4, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s);
-      } else {   // short K: weights straight into registers, two blocks per CU overlap their epilogues
-        const dim3 grid(((p.N + 255) / 256) * max_tiles);
-        if (p.w_tiled) expert_gemm_mfma_da<false, true><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0, info);
-        else expert_gemm_mfma_da<false, false><<<grid, dim3(256), 0, s>>>(p, tile_e, tile_r0, info);
+      if constexpr (GEMM1) {   // long K: the LDS ring of copies
+        launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
+      } else if (p.w_tiled) {   // short K, fragment-order weights: straight into registers, two blocks per CU
+        expert_gemm_mfma_da<false, true><<<dim3(((p.N + 255) / 256) * max_tiles), dim3(256), 0, s>>>(p, tile_e,
+                                                                                                    tile_r0, info);
+      } else {   // stored layout: the paired ring (measured at M = 8192: 644 us, against 728 us in registers; on
+                 // the fragment-order copy the register kernel wins, 625 against 662 us)
+        launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
       }
       break;
     case W_FP8_BLOCK32: launch_mfma_tn<W_FP8_BLOCK32, GEMM1, 256>(p, max_tiles, tile_e, tile_r0, info, s); break;
