@@ -169,6 +169,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(int P, int E, const
 // k experts are distinct, so expert e's pairs are one per token: bit t of the LDS mask of expert e says
 // that token t chose it. The count is the mask's popcount, and the stable rank of pair (t, j) inside its
 // expert is the number of set bits below t. One wave scans the counts; no per-pair sweep.
+template <int NJ>
 __global__ __launch_bounds__(1024) void select_permute_small_kernel(
     int M, int E, int k, float route_scale, int nparts, const float* __restrict__ logits,
     const float* __restrict__ gate_b, int32_t* __restrict__ ids, float* __restrict__ rw, int32_t* __restrict__ counts,
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
   if (tid < 256) emask[tid] = 0ull;
   __syncthreads();
   for (int t = wave; t < M; t += kSmallPairs / 64)
-    select_token(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, sid, emask);
+    select_token<NJ>(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, sid, emask);
   __syncthreads();
   if (wave == 0) {   // counts, offsets and the active list: lane l owns experts 4l .. 4l + 3
     int c[4], csum = 0, fsum = 0;
@@ -238,9 +239,13 @@ void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* 
 void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
                                  const float* gate_b, int32_t* ids, float* rw, int32_t* counts,
                                  int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s) {
-  select_permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, router_logit_parts(M, H),
-                                                                     logits, gate_b, ids, rw, counts, offsets, pairs,
-                                                                     inv, active);
+  const int parts = router_logit_parts(M, H);
+  if (E <= 128)
+    select_permute_small_kernel<2><<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, parts, logits, gate_b,
+                                                                         ids, rw, counts, offsets, pairs, inv, active);
+  else
+    select_permute_small_kernel<4><<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, parts, logits, gate_b,
+                                                                         ids, rw, counts, offsets, pairs, inv, active);
 }
 
 }  // namespace moe

@@ -198,6 +198,7 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
 
 // One wave per token, four tokens per block: scores, biased top-k, normalisation; at M > 64 the wave
 // also QDQs the token's row (one 32-wide block per lane per pass); at M <= 64 the logits kernel has.
+template <int NJ>
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
                                                          int nparts, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
                                                          uint8_t* __restrict__ x_q, uint8_t* __restrict__ x_s) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= M) return;
-  select_token(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, nullptr, nullptr);
+  select_token<NJ>(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, nullptr, nullptr);
   if (M <= kSmallM) return;
   const int nb = H / 32;
   for (int b = lane; b < nb; b += 64)
@@ -230,8 +231,13 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
                               uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  router_select_qdq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, router_logit_parts(M, H),
-                                                            logits, gate_b, x, ids, rw, x_q, x_s);
+  const int parts = router_logit_parts(M, H);
+  if (E <= 128)
+    router_select_qdq<2><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, logits, gate_b, x, ids,
+                                                                 rw, x_q, x_s);
+  else
+    router_select_qdq<4><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, logits, gate_b, x, ids,
+                                                                 rw, x_q, x_s);
 }
 
 }  // namespace moe

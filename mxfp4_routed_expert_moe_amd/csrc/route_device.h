@@ -53,7 +53,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // One wave selects the experts of token t from the partial logit planes [nparts][M][E] (added in
 // ascending plane order). Lane 0 writes ids[t * k + r] and rw[t * k + r] (r = rank, descending
 // selection score); when sid is given, the ids to sid[t * k + r] too, and when emask is given (t < 64)
-// it sets bit t of emask[id] for each chosen expert. The k ids of a token are distinct. E <= 256, k <= 8.
+// it sets bit t of emask[id] for each chosen expert. The k ids of a token are distinct. k <= 8; NJ experts
+// per lane, E <= 64 * NJ (NJ = 2 for E <= 128 halves the per-lane work; the decisions do not depend on NJ).
+template <int NJ>
 __device__ __forceinline__ void select_token(int t, int M, int E, int k, float route_scale, int nparts,
                                              const float* __restrict__ logits, const float* __restrict__ gate_b,
                                              int lane, int32_t* __restrict__ ids, float* __restrict__ rw,
@@ -61,9 +63,9 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
   // scores and selection values: lane owns experts lane, lane + 64, ... Every partial logit load is
   // issued before the first is used; the planes are then added in ascending order.
   const size_t plane = (size_t)M * E;
-  float pv[4][kMaxLogitParts], bias[4];
+  float pv[NJ][kMaxLogitParts], bias[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     bias[j] = 0.0f;
     if (e < E) {
@@ -73,10 +75,10 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
       bias[j] = gate_b[e];
     }
   }
-  float sc[4];
-  uint32_t key[4];   // selection order as one unsigned key: ordered fp32 bits of the selection score
+  float sc[NJ];
+  uint32_t key[NJ];   // selection order as one unsigned key: ordered fp32 bits of the selection score
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     sc[j] = 0.0f;
     key[j] = 0u;   // below every real candidate
@@ -101,7 +103,7 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
     if (r >= k) continue;
     uint64_t best = 0;   // (key << 32) | (0xFFFFFFFF - expert id)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint64_t c = ((uint64_t)key[j] << 32) | (0xFFFFFFFFu - uint32_t(lane + 64 * j));
       if (c > best) best = c;
     }
@@ -110,12 +112,12 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
     const int jw = win >> 6;
     float mine = sc[0];
 #pragma unroll
-    for (int j = 1; j < 4; ++j)
+    for (int j = 1; j < NJ; ++j)
       if (jw == j) mine = sc[j];
     wsel[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), win & 63));
     isel[r] = win;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
       if (lane + 64 * j == win) key[j] = 0u;   // remove the winner
   }
   if (lane == 0) {
