@@ -22,32 +22,18 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Maximum of a 64-bit value over the 64 lanes of the wave, returned to every lane (wave-uniform).
+// Maximum of a 32-bit value over the 64 lanes of the wave, returned to every lane (wave-uniform).
 // Inside each 16-lane row: DPP exchanges with the lane at xor 1 and xor 2 (quad permutes), then with the
 // mirrored lane in the 8-lane half and in the row, each step taking the larger value, so every lane
 // ends with its row's maximum; then the four row maxima are read as scalars.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#define MOE_DPP_MAX_STEP(ctrl)                                                                        \
-  {                                                                                                   \
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false);  \
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false); \
-    const uint64_t o = ((uint64_t)ohi << 32) | olo;                                                   \
-    if (o > v) v = o;                                                                                 \
-  }
-  MOE_DPP_MAX_STEP(0xB1)    // quad_perm [1, 0, 3, 2]
-  MOE_DPP_MAX_STEP(0x4E)    // quad_perm [2, 3, 0, 1]
-  MOE_DPP_MAX_STEP(0x141)   // row_half_mirror
-  MOE_DPP_MAX_STEP(0x140)   // row_mirror
-#undef MOE_DPP_MAX_STEP
-  uint64_t m = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * row);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * row);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    if (o > m) m = o;
-  }
-  return m;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1, 0, 3, 2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2, 3, 0, 1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  const uint32_t m01 = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t m23 = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(m01, m23);
 }
 
 // One wave selects the experts of token t from the partial logit planes [nparts][M][E] (added in
@@ -92,8 +78,8 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
       key[j] = ordered_key(sc[j] + bias[j]);
     }
   }
-  // k rounds of a wave-wide maximum of (key, -expert id): the larger selection score wins, equal
-  // scores go to the lower expert id; the winner's lane then hands over its unbiased score
+  // k rounds of a wave-wide maximum: the larger selection score wins, equal scores go to the lower
+  // expert id; the winner's lane then hands over its unbiased score
   float wsel[8];
   int isel[8];
 #pragma unroll
@@ -101,14 +87,18 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
     wsel[r] = 0.0f;
     isel[r] = 0;
     if (r >= k) continue;
-    uint64_t best = 0;   // (key << 32) | (0xFFFFFFFF - expert id)
+    // the largest key over the wave, then its lowest expert id (id = lane + 64 j: the smallest j that holds
+    // it, then the lowest lane): the same order as a maximum of (key, -id) pairs, in 32-bit steps
+    uint32_t best = key[0];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint64_t c = ((uint64_t)key[j] << 32) | (0xFFFFFFFFu - uint32_t(lane + 64 * j));
-      if (c > best) best = c;
+    for (int j = 1; j < NJ; ++j) best = max(best, key[j]);
+    best = wave_max_u32(best);
+    int win = 0;
+#pragma unroll
+    for (int j = NJ - 1; j >= 0; --j) {
+      const unsigned long long hit = __ballot(key[j] == best);
+      if (hit != 0ull) win = 64 * j + (__ffsll(hit) - 1);
     }
-    best = wave_max_u64(best);
-    const int win = int(0xFFFFFFFFu - uint32_t(best));
     const int jw = win >> 6;
     float mine = sc[0];
 #pragma unroll
