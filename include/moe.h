@@ -235,7 +235,9 @@ size_t moe_mxfp4_tiled_weights_bytes(const moe_dims* dims);
  * lane l of the block-scaled matrix-core instruction (lane l: row l % 16, inputs 32 (l / 16) .. + 31).
  * Done once (e.g. when the weights are loaded). out: device, 16-byte aligned,
  * moe_mxfp4_tiled_weights_bytes(dims) bytes, owned by the caller; must not overlap w's weights.
- * w's scale pointers and w->stage_scales / w->tiled_weights are not read. */
+ * w's scale pointers and w->stage_scales / w->tiled_weights are not read. Errors (nothing enqueued):
+ * MOE_ERR_INVALID_ARG for NULL or misaligned w1, w3, w2 or out, or an out that overlaps them;
+ * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for dims outside the supported domain. */
 moe_status moe_prepare_mxfp4_weights(const moe_dims* dims, const moe_mxfp4_experts* w, uint8_t* out, void* stream);
 
 /* Expand one packed MXFP4 matrix (or a stack of them) to bf16: w uint8 [rows, cols/2], s uint8
