@@ -227,7 +227,8 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 // a contiguous run of bytes), prefetching kStreamU steps ahead, so the only vector-memory traffic in
 // the loop is the wave's own weight rows. The E8M0 scales of the 64 rows and up to 4 activation rows
 // of the expert (E4M3 codes and scales) are staged in LDS at the start; experts with more rows are
-// processed 4 rows at a time. The four fragments meet in LDS for the epilogue.
+// processed 4 rows at a time. GEMM1's w1 and w3 fragments meet in LDS for the SwiGLU/QDQ epilogue, which
+// two waves share; GEMM2's waves store their own rows.
 //
 // Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E2M1 operand
 // holds K [32g, 32g + 32) of the 128-wide step (one stored 16-byte MX block); an E4M3 operand holds
@@ -292,7 +293,7 @@ struct StreamA<W_FP8_BLOCK32> {
 }  // namespace
 
 // Dynamic LDS: scales [64][K/32], activation codes [4][K], activation scales [4][K/32], then the
-// [4 waves][64 lanes] fp32x4 exchange of the fragments.
+// [4 waves][64 lanes] fp32x4 exchange of the fragments and the [2][16] amax halves (GEMM1).
 template <int WF, bool GEMM1, bool TILED>
 __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   static_assert(!TILED || WF == W_MXFP4, "the fragment-order copy holds MXFP4 codes");
@@ -314,6 +315,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   uint8_t* xb = sc + 64 * KB;                          // [4][K]
   uint8_t* xsb = xb + kStreamRows * K;                 // [4][KB]
   f32x4* xch = reinterpret_cast<f32x4*>(dyn + ((64 * KB + kStreamRows * (K + KB) + 15) & ~15));   // [4][64]
+  float* amx = reinterpret_cast<float*>(xch + 4 * 64);                                            // [2][16]
   // block rows: GEMM1 output columns c0 .. c0 + 31 (LDS rows 0..31 = w1, 32..63 = w3); GEMM2 rows c0 .. c0 + 63
   const int c0 = GEMM1 ? blockIdx.x * 32 : blockIdx.x * 64;
   auto grow_of = [&](int r) { return GEMM1 ? c0 + (r & 31) : c0 + r; };
@@ -411,56 +413,50 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
       for (int u = 0; u < kStreamU; ++u) A[u].template load<kKStride>(wsrc, min(ks0 + 2 * kStreamU + u, nk - 1));
       run(Bs, ks0 + kStreamU);
     }
-    // the four fragments meet in LDS; wave 0 runs the epilogue (lane: weight rows 4g..4g+3, row r16)
-    xch[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-      const f32x4 a0 = xch[lane], a1 = xch[64 + lane], a2 = xch[128 + lane], a3 = xch[192 + lane];
-      const bool valid = r16 < n;
-      const int pos = row0 + tg + r16;
-      if constexpr (GEMM1) {
+    // epilogue (lane: weight rows 4g..4g+3 of its fragment, activation row r16)
+    const bool valid = r16 < n;
+    const int pos = row0 + tg + r16;
+    if constexpr (GEMM1) {
+      // waves 0 and 1 each finish 16 of the block's 32 output columns: g from their own w1 fragment, u from
+      // the w3 fragment of wave + 2 (through LDS); the amax of the 32-column QDQ block meets in LDS
+      xch[wave * 64 + lane] = acc;
+      __syncthreads();
+      float h[4];
+      if (wave < 2) {
+        const f32x4 gf = xch[wave * 64 + lane], uf = xch[(wave + 2) * 64 + lane];
         float rwv = 1.0f;
         if (valid && !p.dense) rwv = p.rw[p.pairs[pos]];
-        const f32x4 gf[2] = {a0, a1}, uf[2] = {a2, a3};
-        float h[2][4];
         float amax = 0.0f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            h[half][v] = round_bf16(swiglu(round_bf16(gf[half][v]), round_bf16(uf[half][v]), rwv, !p.dense));
-            amax = fmaxf(amax, fabsf(h[half][v]));
-          }
-        // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
+        for (int v = 0; v < 4; ++v) {
+          h[v] = round_bf16(swiglu(round_bf16(gf[v]), round_bf16(uf[v]), rwv, !p.dense));
+          amax = fmaxf(amax, fabsf(h[v]));
+        }
+        // this wave's 16 columns of row r16 live in lanes r16 + 16 g, g = 0..3
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const int E8 = qdq_exponent(amax);
+        if (g == 0) amx[wave * 16 + r16] = amax;
+      }
+      __syncthreads();
+      if (wave < 2) {
+        const int E8 = qdq_exponent(fmaxf(amx[r16], amx[16 + r16]));
         const float inv = exp2_neg(E8);
         if (valid) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const uint32_t packed = qdq_code4(h[half][0], h[half][1], h[half][2], h[half][3], inv);
-            *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + c0 + 16 * half + 4 * g) = packed;
-          }
-          if (g == 0) p.h_s[(size_t)pos * (p.N / 32) + c0 / 32] = uint8_t(E8 + 127);
+          *reinterpret_cast<uint32_t*>(p.h_q + (size_t)pos * p.N + c0 + 16 * wave + 4 * g) =
+              qdq_code4(h[0], h[1], h[2], h[3], inv);
+          if (wave == 0 && g == 0) p.h_s[(size_t)pos * (p.N / 32) + c0 / 32] = uint8_t(E8 + 127);
         }
-      } else {
-        if (valid) {
-          const int orow = p.dense ? pos : p.pairs[pos];
-          const f32x4 af[4] = {a0, a1, a2, a3};
-          if (p.out_f32) {
-            float* o = p.out_f32 + (size_t)orow * p.N + c0 + 4 * g;
-#pragma unroll
-            for (int f = 0; f < 4; ++f) *reinterpret_cast<f32x4*>(o + 16 * f) = af[f];
-          } else {
-            uint16_t* o = p.out + (size_t)orow * p.N + c0 + 4 * g;
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-              const uint32_t lo = uint32_t(f32_to_bf16_rne(af[f][0])) | (uint32_t(f32_to_bf16_rne(af[f][1])) << 16);
-              const uint32_t hi = uint32_t(f32_to_bf16_rne(af[f][2])) | (uint32_t(f32_to_bf16_rne(af[f][3])) << 16);
-              *reinterpret_cast<u32x2*>(o + 16 * f) = u32x2{lo, hi};
-            }
-          }
+      }
+    } else {
+      // each wave holds the whole inner dimension of its 16 rows: it stores them itself
+      if (valid) {
+        const int orow = p.dense ? pos : p.pairs[pos];
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4*>(p.out_f32 + (size_t)orow * p.N + c0 + 16 * wave + 4 * g) = acc;
+        } else {
+          const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[0])) | (uint32_t(f32_to_bf16_rne(acc[1])) << 16);
+          const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[2])) | (uint32_t(f32_to_bf16_rne(acc[3])) << 16);
+          *reinterpret_cast<u32x2*>(p.out + (size_t)orow * p.N + c0 + 16 * wave + 4 * g) = u32x2{lo, hi};
         }
       }
     }
@@ -470,7 +466,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
 
 size_t stream_lds_bytes(int K) {
   const int KB = K / 32;
-  return (size_t)((64 * KB + kStreamRows * (K + KB) + 15) & ~15) + 4 * 64 * sizeof(f32x4);
+  return (size_t)((64 * KB + kStreamRows * (K + KB) + 15) & ~15) + 4 * 64 * sizeof(f32x4) + 32 * sizeof(float);
 }
 
 template <bool GEMM1>
