@@ -19,7 +19,8 @@
 // cuts LDS bytes per MFMA). K steps of 128 stream into an LDS ring by direct global-to-LDS copies, with
 // XOR-swizzled 16-byte chunks (conflict-free fragment reads): for MXFP4 weights a two-stage ring and two
 // blocks per CU, whose waves share the SIMDs and overlap each other's copies, fragment reads and MFMAs;
-// for FP8 weights a three-stage ring issued two stages ahead, one block per CU. The rows of
+// for FP8 weights a three-stage ring issued two stages ahead, one block per CU. (MXFP4 weights in the
+// fragment-order copy go to the second kernel below, which loads them straight into registers.) The rows of
 // an expert are its sorted positions offsets[e] .. offsets[e+1]; GEMM1 gathers the activation row of
 // each position's token, GEMM2 reads the QDQ'd h rows in sorted order and scatters y to the pair's slot
 // row. The (expert, row tile) of a block comes from a tile list built on the device from the expert
@@ -741,17 +742,22 @@ static void launch_mfma_tn(const GemmProblem& p, int max_tiles, const int32_t* t
   expert_gemm_mfma<WF, GEMM1, TN, false, PAIR><<<dim3(cols * rows), dim3(TN), 0, s>>>(p, tile_e, tile_r0, info);
 }
 
-// MXFP4 weights, GEMM1: 256 weight rows per block, two blocks per CU (measured at M = 8192: 1.20 ms, against
-// 1.29 ms for 512-row blocks of 8 waves with a three-stage ring, one block per CU). GEMM2: see below. FP8
-// weights (twice the bytes per row): 256 rows, one block per CU.
+// MXFP4 weights on the fragment-order copy: both GEMMs load the weights straight into registers (measured at
+// M = 8192, interleaved with the ring kernel: GEMM1 1.17-1.19 ms against 1.22-1.23 ms; GEMM2 625 against
+// 662 us). On the stored layout the paired ring serves both: GEMM1 256 weight rows per block, two blocks per
+// CU (1.20 ms, against 1.29 ms for 512-row blocks of 8 waves with a three-stage ring, one block per CU).
+// FP8 weights (twice the bytes per row): 256 rows, one block per CU.
 template <bool GEMM1>
 static void launch_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
                         const int32_t* tile_r0, const int32_t* info, hipStream_t s) {
   switch (f) {
     case W_MXFP4:
-      if constexpr (GEMM1) {   // long K: the LDS ring of copies
-        launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
-      } else if (p.w_tiled) {   // short K, fragment-order weights: straight into registers, two blocks per CU
+      if constexpr (GEMM1) {
+        if (p.w_tiled)
+          expert_gemm_mfma_da<true, true><<<dim3((p.N / 128) * max_tiles), dim3(256), 0, s>>>(p, tile_e, tile_r0, info);
+        else   // long K on the stored layout: the LDS ring of copies
+          launch_mfma_tn<W_MXFP4, GEMM1, 256, true>(p, max_tiles, tile_e, tile_r0, info, s);
+      } else if (p.w_tiled) {   // fragment-order weights: straight into registers, two blocks per CU
         expert_gemm_mfma_da<false, true><<<dim3(((p.N + 255) / 256) * max_tiles), dim3(256), 0, s>>>(p, tile_e,
                                                                                                     tile_r0, info);
       } else {   // stored layout: the paired ring (measured at M = 8192: 644 us, against 728 us in registers; on
