@@ -35,7 +35,8 @@ void launch_qdq_rows(int M, int K, const uint16_t* x, uint8_t* xq, uint8_t* xs, 
 
 namespace {
 
-constexpr int kDenseInFlight = 2;       // K steps of weight loads in flight per wave (2 beat 3, 4 and 8)
+constexpr int kDenseInFlight = 1;       // K steps per weight register set (two sets take turns; 1 beat 2 and 4)
+constexpr int kDenseWaitVmLgkm0 = 0x7 << 4;   // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(0)
 constexpr int kDenseBlocks = 1024;      // blocks the K split aims for
 constexpr int kDenseMinSteps = 4;       // fewest K steps per run
 
@@ -89,14 +90,21 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
   f32x4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Weight loads: two register sets of U K steps take turns, so one set's loads are in flight while the
+  // other's MFMAs run. Loads are never guarded by a condition (past the run's last step they re-read it),
+  // and the sets are never copied into each other: either would make the compiler wait for every load in
+  // flight before the first MFMA of a set, not just for that set's own.
   constexpr int U = kDenseInFlight;
-  u32x4 A0[U], A1[U];
+  u32x4 PA[U], PB[U], QA[U], QB[U];
+  auto load = [&](u32x4 (&RA)[U], u32x4 (&RB)[U], int j) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int ks = lo + min(u, ns - 1);
-    A0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
-    A1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
-  }
+    for (int u = 0; u < U; ++u) {
+      const int ks = lo + min(j + u, ns - 1);
+      RA[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
+      RB[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
+    }
+  };
+  load(PA, PB, 0);
   if (x != nullptr) {   // bf16 rows given: QDQ this run's 32-wide blocks straight into LDS (thread per block)
     const int nb = ns * 4;
     for (int i = threadIdx.x; i < M * nb; i += 256) {
@@ -108,22 +116,16 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
       xsb[t * SL + j] = sc;
     }
   }
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int j0 = 0; j0 < ns; j0 += U) {
-    u32x4 B0[U], B1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (j0 + U + u < ns) {
-        const int ks = lo + j0 + U + u;
-        B0[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
-        B1[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
-      }
+  // staging done (the builtin wait, unlike one in asm, is seen by the compiler's wait placement), then meet
+  __builtin_amdgcn_s_waitcnt(kDenseWaitVmLgkm0);
+  __syncthreads();
+  auto run = [&](const u32x4 (&RA)[U], const u32x4 (&RB)[U], int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
       if (j < ns) {
-        const i32x8 Af = i32x8{(int)A0[u][0], (int)A0[u][1], (int)A0[u][2], (int)A0[u][3],
-                               (int)A1[u][0], (int)A1[u][1], (int)A1[u][2], (int)A1[u][3]};
+        const i32x8 Af = i32x8{(int)RA[u][0], (int)RA[u][1], (int)RA[u][2], (int)RA[u][3],
+                               (int)RB[u][0], (int)RB[u][1], (int)RB[u][2], (int)RB[u][3]};
         const int sa = wsb[(wave >> 1) * SL + 4 * j + g];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -139,11 +141,12 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      A0[u] = B0[u];
-      A1[u] = B1[u];
-    }
+  };
+  for (int j0 = 0; j0 < ns; j0 += 2 * U) {
+    load(QA, QB, j0 + U);
+    run(PA, PB, j0);
+    load(PA, PB, j0 + 2 * U);
+    run(QA, QB, j0 + U);
   }
   // lane: weight rows n0 + 16 wave + 4g .. + 3 of token 16 q + r16
   const int n = n0 + 16 * wave + 4 * g;
