@@ -56,6 +56,16 @@ def test_dense_ragged_token_groups(M):
     assert_within(bf16_host(y), ref["y"], f"wq_a M={M}")
 
 
+@pytest.mark.parametrize("M", [5, 20])
+def test_dense_single_run_wide_shape(M):
+    """16384 output rows (a block per CU already): the whole K in one run and no reduce launch, with a
+    partial 16-token group."""
+    y, y32, ref, rows = _run(16384, 1280, M, seed=100 + M)
+    assert_within(bf16_host(y), ref["y"], f"wq_b M={M}")
+    b = F.bf16_bits(F.bf16_rne(y32.cpu().numpy().astype(np.float64)))
+    assert np.array_equal(b, y.cpu().numpy().view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [65, 300])
 def test_dense_prefill_width(M):
     """Above 64 rows: the block-scaled grouped GEMM as one expert."""
