@@ -314,8 +314,9 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
     return res
 
 
-def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30) -> dict:
-    """The dense FP8 projection family at decode width: moe_fp8_linear per shape, with the weights in as
+def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30, tiled: bool = True) -> dict:
+    """The dense FP8 projection family at decode width: moe_fp8_linear per shape (by default on the
+    fragment-order copy of the weights made at load, moe_fp8_linear_tiled), with the weights in as
     many replicas as fill about 1 GiB (rotated, so the 256 MB last-level cache cannot serve them). The
     calls are captured once in a HIP graph (the library is graph-safe) and the replays timed with HIP
     events, so host launch overhead does not enter the per-call time."""
@@ -331,21 +332,33 @@ def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30) -> dict
         x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
         replicas = max(4, -(-pool_bytes // (N * K)))
         w0, s0 = torch.from_numpy(inp["w"]).cuda(), torch.from_numpy(inp["s"]).cuda()
-        ws_ = [(w0.clone(), s0.clone()) for _ in range(replicas)]
+        if tiled:
+            ws_ = [(moe.moe_prepare_fp8_weights(w0), s0.clone()) for _ in range(replicas)]
+        else:
+            ws_ = [(w0.clone(), s0.clone()) for _ in range(replicas)]
+        torch.cuda.synchronize()
         y = torch.empty((M, N), dtype=torch.int16, device="cuda")
         work = moe.fp8_linear_workspace(M, N, K)
+
+        def call(i):
+            w_i, s_i = ws_[i % replicas]
+            if tiled:
+                moe.moe_fp8_linear_tiled(x, w_i, N, s_i, y=y, ws=work)
+            else:
+                moe.moe_fp8_linear(x, w_i, s_i, y=y, ws=work)
+
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(replicas):
-                moe.moe_fp8_linear(x, *ws_[i % replicas], y=y, ws=work)
+                call(i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         per_graph = replicas
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(per_graph):
-                moe.moe_fp8_linear(x, *ws_[i % replicas], y=y, ws=work)
+                call(i)
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -362,7 +375,8 @@ def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30) -> dict
                          hbm_frac=round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4))
         del ws_, work, w0, s0
     torch.cuda.empty_cache()
-    return dict(workload=f"dense FP8 projections at M={M}", bound="hbm", unit="GB/s", shapes=out)
+    return dict(workload=f"dense FP8 projections at M={M}", bound="hbm", unit="GB/s",
+                weight_layout="fragment-order" if tiled else "stored row-major", shapes=out)
 
 
 def calibrate_copy(gib: int = 1, reps: int = 5) -> dict:
@@ -413,8 +427,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
     ap.add_argument("--no-widths", action="store_true", help="skip the verifier widths M = 1 .. 32")
     ap.add_argument("--stored-layout", action="store_true",
-                    help="stream the weight codes from their stored row-major layout instead of the fragment-order "
-                         "copy made at load")
+                    help="stream the weight codes (routed experts and the dense FP8 family) from their stored "
+                         "row-major layout instead of the fragment-order copy made at load")
     ap.add_argument("--dense-only", action="store_true",
                     help="only the dense FP8 projection family (prints its object as the JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -435,7 +449,7 @@ def main():
         print(json.dumps({"calibrate_copy": calibrate_copy()}), flush=True)
         return
     if args.dense_only:
-        print(json.dumps({"dense_fp8": measure_dense()}), flush=True)
+        print(json.dumps({"dense_fp8": measure_dense(tiled=not args.stored_layout)}), flush=True)
         return
     widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
     tiled = not args.stored_layout
@@ -458,7 +472,7 @@ def main():
                        layer_tflops=round(p["layer_tflops"], 1), roofline=p["roofline"])
     dense = None
     if not args.no_dense:
-        dense = measure_dense()
+        dense = measure_dense(tiled=not args.stored_layout)
         summary = ", ".join(f"{k}: {v['us']} us" for k, v in dense["shapes"].items())
         print(f"# dense: {summary}", file=sys.stderr, flush=True)
     cpu = None

@@ -210,6 +210,25 @@ size_t moe_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, const uint8_t* s,
                           uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of moe_prepare_fp8_weights output: N * K (0 for a shape moe_fp8_linear refuses). */
+size_t moe_fp8_tiled_weights_bytes(int32_t N, int32_t K);
+
+/* One-time re-layout of a dense FP8 weight matrix (the operand of section 4 "Dense") for the decode-width
+ * kernel: w uint8 E4M3 [N, K] row-major -> out[f][q][l][b] = w[16 f + l % 16][64 q + 16 (l / 16) + b]
+ * (f < N / 16 row fragments, q < K / 64 chunks of 64 bytes, lane l < 64, byte b < 16), so that every weight
+ * load of a wave reads 1 KB of consecutive bytes. Same values in another order, done once (e.g. at load).
+ * w and out: device, 16-byte aligned, not overlapping; out holds moe_fp8_tiled_weights_bytes(N, K) bytes
+ * and is owned by the caller. Errors: INVALID_ARG (NULL, misaligned or overlapping pointers),
+ * UNSUPPORTED (a shape moe_fp8_linear refuses). */
+moe_status moe_prepare_fp8_weights(int32_t N, int32_t K, const uint8_t* w, uint8_t* out, void* stream);
+
+/* moe_fp8_linear with the weights given as the moe_prepare_fp8_weights copy (w_tiled), for decode widths:
+ * M <= 64, UNSUPPORTED above (the prefill-width kernel reads the row-major codes). Outputs are bit-identical
+ * to moe_fp8_linear's on the same inputs; same scales s, workspace and errors otherwise. */
+moe_status moe_fp8_linear_tiled(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w_tiled,
+                                const uint8_t* s, uint16_t* y, float* y_f32, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Bytes of moe_prepare_mxfp4_scales output: 3 * E * I * H / 32 (0 if dims are invalid). */
 size_t moe_mxfp4_stage_scales_bytes(const moe_dims* dims);
 

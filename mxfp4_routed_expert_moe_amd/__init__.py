@@ -21,7 +21,8 @@ __all__ = [
     "moe_expert_gemm1", "moe_expert_gemm2", "moe_shared_expert", "moe_combine", "moe_forward", "moe_expand_mxfp4", "workspace",
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
     "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
-    "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights",
+    "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights", "moe_fp8_tiled_weights_bytes",
+    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -96,6 +97,12 @@ lib.moe_fp8_linear_workspace_bytes.argtypes = [_I32, _I32, _I32]
 lib.moe_fp8_linear_workspace_bytes.restype = _SZ
 lib.moe_fp8_linear.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_fp8_linear.restype = _I32
+lib.moe_fp8_linear_tiled.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+lib.moe_fp8_linear_tiled.restype = _I32
+lib.moe_fp8_tiled_weights_bytes.argtypes = [_I32, _I32]
+lib.moe_fp8_tiled_weights_bytes.restype = _SZ
+lib.moe_prepare_fp8_weights.argtypes = [_I32, _I32, _P, _P, _P]
+lib.moe_prepare_fp8_weights.restype = _I32
 lib.moe_mxfp4_stage_scales_bytes.argtypes = [ctypes.POINTER(_Dims)]
 lib.moe_mxfp4_stage_scales_bytes.restype = _SZ
 lib.moe_prepare_mxfp4_scales.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_MXFP4), _P, _P]
@@ -396,3 +403,32 @@ def moe_fp8_linear(x, w, s, y=None, y_f32=None, ws=None, stream=None):
     st = lib.moe_fp8_linear(M, N, K, _ptr(x, _BF), _ptr(w, torch.uint8), _ptr(s, torch.uint8), _ptr(y, _BF),
                             _ptr(y_f32, torch.float32), _ptr(ws, torch.uint8), ws.numel(), _stream(stream))
     _check(st, "moe_fp8_linear")
+
+
+def moe_fp8_tiled_weights_bytes(N: int, K: int) -> int:
+    return int(lib.moe_fp8_tiled_weights_bytes(N, K))
+
+
+def moe_prepare_fp8_weights(w, out=None, stream=None) -> torch.Tensor:
+    """The fragment-order copy of a dense FP8 weight matrix w uint8 [N, K] (into out, or a new uint8 tensor
+    of N * K bytes on w's device)."""
+    N, K = w.shape
+    n = moe_fp8_tiled_weights_bytes(N, K)
+    if n == 0:
+        raise MoeError("unsupported dense linear shape")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    st = lib.moe_prepare_fp8_weights(N, K, _ptr(w, torch.uint8), _ptr(out, torch.uint8), _stream(stream))
+    _check(st, "moe_prepare_fp8_weights")
+    return out
+
+
+def moe_fp8_linear_tiled(x, w_tiled, N, s, y=None, y_f32=None, ws=None, stream=None):
+    """moe_fp8_linear with the moe_prepare_fp8_weights copy of the [N, K] weights (decode widths, M <= 64)."""
+    M, K = x.shape
+    if ws is None:
+        ws = fp8_linear_workspace(M, N, K, device=x.device)
+    st = lib.moe_fp8_linear_tiled(M, N, K, _ptr(x, _BF), _ptr(w_tiled, torch.uint8), _ptr(s, torch.uint8),
+                                  _ptr(y, _BF), _ptr(y_f32, torch.float32), _ptr(ws, torch.uint8), ws.numel(),
+                                  _stream(stream))
+    _check(st, "moe_fp8_linear_tiled")

@@ -56,6 +56,10 @@ __device__ __forceinline__ void dense_run(uint8_t* lds, const uint8_t* src, int 
 
 // Dynamic LDS: activation codes [M][S * 128], activation scales [M][S * 4], weight scales [2][S * 4]
 // (S = steps of this run).
+// TILED: w is the fragment-order copy ([N / 16][K / 64][64 lanes][16 bytes]: lane l of chunk q holds bytes
+// 64 q + 16 (l / 16) .. + 15 of row 16 f + l % 16), so each weight load of a wave reads 1 KB of consecutive
+// bytes instead of 64-byte pieces of 16 rows.
+template <bool TILED>
 __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, int steps_per_run,
                                                          const uint16_t* __restrict__ x,
                                                          const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
@@ -85,7 +89,10 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
     if (mine()) dense_run<4>(wsb + SL, s + (size_t)(n0 / 32 + 1) * KB + lo * 4, ns * 4, lane);
   }
   // the first weight steps are in flight while the activations are staged
-  const uint8_t* wrow = w + (size_t)(n0 + 16 * wave + r16) * K;
+  // lane's bytes of a step: wsrc + ks * kStepBytes (first 16) and + kHalf (second 16)
+  constexpr int kStepBytes = TILED ? 2048 : 128, kHalf = TILED ? 1024 : 64;
+  const uint8_t* wsrc = TILED ? w + (size_t)((n0 + 16 * wave) / 16) * (size_t)(K / 64) * 1024 + 16 * lane
+                              : w + (size_t)(n0 + 16 * wave + r16) * K + 16 * g;
   const int nt = (M + 15) / 16;   // 16-token groups (the MFMA's B columns)
   f32x4 acc[4];
 #pragma unroll
@@ -100,8 +107,8 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = lo + min(j + u, ns - 1);
-      RA[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 16 * g);
-      RB[u] = *reinterpret_cast<const u32x4*>(wrow + ks * 128 + 64 + 16 * g);
+      RA[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes);
+      RB[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes + kHalf);
     }
   };
   load(PA, PB, 0);
@@ -214,18 +221,24 @@ DensePlan dense_plan(int M, int N, int K) {
 }
 
 void launch_fp8_linear_stream(int M, int N, int K, const uint16_t* x, const uint8_t* xq, const uint8_t* xs,
-                              const uint8_t* w, const uint8_t* s, float* part, uint16_t* y, float* y32,
+                              const uint8_t* w, bool w_tiled, const uint8_t* s, float* part, uint16_t* y, float* y32,
                               hipStream_t st) {
   const DensePlan pl = dense_plan(M, N, K);
   dim3 grid(N / 64, pl.runs);
+  auto stream = [&](float* pp, uint16_t* yy, float* yy32) {
+    if (w_tiled)
+      fp8_linear_stream<true><<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, pp, yy, yy32);
+    else
+      fp8_linear_stream<false><<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, pp, yy,
+                                                                yy32);
+  };
   if (pl.runs > 1) {
-    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, part, nullptr,
-                                                       nullptr);
+    stream(part, nullptr, nullptr);
     const long long n4 = (long long)M * N / 4;
     const int rg = (int)std::min<long long>((n4 + 255) / 256, 4096);
     dense_reduce_kernel<<<dim3(rg), dim3(256), 0, st>>>(n4, pl.runs, (long long)M * N, part, y, y32);
   } else {
-    fp8_linear_stream<<<grid, dim3(256), pl.lds, st>>>(M, N, K, pl.steps_per_run, x, xq, xs, w, s, nullptr, y, y32);
+    stream(nullptr, y, y32);
   }
 }
 

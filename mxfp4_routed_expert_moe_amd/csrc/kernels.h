@@ -122,9 +122,10 @@ struct DensePlan {
 };
 DensePlan dense_plan(int M, int N, int K);
 // y = bf16(x_hat W^T) (or fp32 into y32) for M <= 64: W FP8 [N, K] with E8M0 [N/32, K/32]; N % 64 == 0.
-// With x (bf16 [M, K]) the blocks QDQ their runs themselves and xq / xs are not read.
+// With x (bf16 [M, K]) the blocks QDQ their runs themselves and xq / xs are not read. w_tiled: w is the
+// fragment-order copy (launch_tile_mxfp4(1, N, 2 K, ...) of the row-major codes).
 void launch_fp8_linear_stream(int M, int N, int K, const uint16_t* x, const uint8_t* xq, const uint8_t* xs,
-                              const uint8_t* w, const uint8_t* s, float* part, uint16_t* y, float* y32,
+                              const uint8_t* w, bool w_tiled, const uint8_t* s, float* part, uint16_t* y, float* y32,
                               hipStream_t st);
 
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,

@@ -576,10 +576,13 @@ size_t moe_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   return std::max<size_t>(linear_layout(M, N, K).total, 256);
 }
 
-moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, const uint8_t* s,
-                          uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+moe_status fp8_linear_impl(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, bool w_tiled,
+                           const uint8_t* s, uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_linear(M, N, K));
   if ((y == nullptr) == (y_f32 == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (w_tiled && M > 64) return MOE_ERR_UNSUPPORTED;   // the fragment-order copy feeds the decode-width kernel
   if (M == 0) return MOE_OK;
   if (!al(x, 16) || !al(w, 16) || !al(s, 16) || !al(ws, 256)) return MOE_ERR_INVALID_ARG;
   if ((y != nullptr && !al(y, 16)) || (y_f32 != nullptr && !al(y_f32, 16))) return MOE_ERR_INVALID_ARG;
@@ -589,7 +592,7 @@ moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, co
   uint8_t* xq = at<uint8_t>(ws, L.xq);
   uint8_t* xs = at<uint8_t>(ws, L.xs);
   if (M <= 64) {   // the blocks QDQ their own runs of x
-    moe::launch_fp8_linear_stream(M, N, K, x, nullptr, nullptr, w, s, at<float>(ws, L.part), y, y_f32, st);
+    moe::launch_fp8_linear_stream(M, N, K, x, nullptr, nullptr, w, w_tiled, s, at<float>(ws, L.part), y, y_f32, st);
   } else {
     moe::launch_qdq_rows(M, K, x, xq, xs, st);
     GemmProblem q{};
@@ -600,6 +603,35 @@ moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, co
     q.out = y; q.out_f32 = y_f32;
     moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, nullptr, nullptr, nullptr, st);
   }
+  return launched();
+}
+
+}  // namespace
+
+moe_status moe_fp8_linear(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w, const uint8_t* s,
+                          uint16_t* y, float* y_f32, void* ws, size_t ws_bytes, void* stream) {
+  return fp8_linear_impl(M, N, K, x, w, false, s, y, y_f32, ws, ws_bytes, stream);
+}
+
+moe_status moe_fp8_linear_tiled(int32_t M, int32_t N, int32_t K, const uint16_t* x, const uint8_t* w_tiled,
+                                const uint8_t* s, uint16_t* y, float* y_f32, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return fp8_linear_impl(M, N, K, x, w_tiled, true, s, y, y_f32, ws, ws_bytes, stream);
+}
+
+size_t moe_fp8_tiled_weights_bytes(int32_t N, int32_t K) {
+  if (check_linear(0, N, K) != MOE_OK) return 0;
+  return (size_t)N * (size_t)K;
+}
+
+moe_status moe_prepare_fp8_weights(int32_t N, int32_t K, const uint8_t* w, uint8_t* out, void* stream) {
+  MOE_TRY(check_linear(0, N, K));
+  if (!al(w, 16) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t n = (size_t)N * (size_t)K;
+  const uintptr_t o = reinterpret_cast<uintptr_t>(out), p = reinterpret_cast<uintptr_t>(w);
+  if (p < o + n && o < p + n) return MOE_ERR_INVALID_ARG;
+  // an E4M3 row of K bytes has the byte layout of an E2M1 row of 2 K values
+  moe::launch_tile_mxfp4(1, N, 2 * K, w, out, static_cast<hipStream_t>(stream));
   return launched();
 }
 

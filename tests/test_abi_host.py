@@ -203,3 +203,28 @@ def test_prepare_tiled_weights_refuses_before_launch(lib):
              ctypes.c_void_p(FAKE + (3 << 32)), None) == INVALID                               # no w3
     assert f(ctypes.byref(Dims(128, 5120, 2300, 6, 1.5)), ctypes.byref(ok), ctypes.c_void_p(FAKE + (3 << 32)),
              None) == UNSUPPORTED
+
+
+def test_dense_fp8_tiled_calls_refuse_before_launch(lib):
+    size = lib.moe_fp8_tiled_weights_bytes
+    size.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    size.restype = ctypes.c_size_t
+    assert size(5120, 15360) == 5120 * 15360                     # same bytes, another order
+    assert size(100, 128) == 0 and size(128, 100) == 0 and size(0, 128) == 0
+    prep = lib.moe_prepare_fp8_weights
+    prep.restype = ctypes.c_int32
+    prep.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    w, out = FAKE, FAKE + (1 << 32)
+    assert prep(1280, 5120, None, out, None) == INVALID
+    assert prep(1280, 5120, w, None, None) == INVALID
+    assert prep(1280, 5120, w + 8, out, None) == INVALID           # misaligned
+    assert prep(1280, 5120, w, w + 1280 * 5120 - 16, None) == INVALID   # out overlaps w
+    assert prep(1280, 5000, w, out, None) == UNSUPPORTED
+    lin = lib.moe_fp8_linear_tiled
+    lin.restype = ctypes.c_int32
+    lin.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    x, s, y, ws = FAKE, FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32)
+    assert lin(65, 1280, 5120, x, w, s, y, None, ws, 1 << 30, None) == UNSUPPORTED   # decode widths only
+    assert lin(8, 1280, 5120, x, w, s, y, y, ws, 1 << 30, None) == INVALID           # both outputs
+    assert lin(8, 1280, 5120, x, w, s, y, None, ws, 16, None) == WORKSPACE
+    assert lin(0, 1280, 5120, x, w, s, y, None, ws, 0, None) == OK                   # empty batch: nothing to do

@@ -84,3 +84,39 @@ def test_dense_small_shapes_and_refusals():
     with pytest.raises(m().MoeError):
         m().moe_fp8_linear(x, w, s, y=torch.empty((2, 128), dtype=torch.int16, device="cuda"),
                            ws=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+
+
+def test_prepare_fp8_weights_layout():
+    """The fragment-order copy: out[f][q][l][b] = w[16 f + l % 16][64 q + 16 (l / 16) + b]."""
+    N, K = 256, 640
+    g = torch.Generator().manual_seed(3)
+    w_host = torch.randint(0, 256, (N, K), dtype=torch.uint8, generator=g)
+    t = m().moe_prepare_fp8_weights(w_host.cuda())
+    torch.cuda.synchronize()
+    want = w_host.numpy().reshape(N // 16, 16, K // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(t.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("name", list(synth.DENSE_SHAPES))
+@pytest.mark.parametrize("M", [1, 8, 37])
+def test_dense_tiled_weights_are_identical(name, M):
+    """moe_fp8_linear_tiled on the prepared copy equals moe_fp8_linear on the row-major codes bit for bit
+    (bf16 and fp32 outputs), at the split-K and single-run plans and a ragged 16-token group."""
+    N, K = synth.DENSE_SHAPES[name]
+    inp = synth.make_dense_inputs(N, K, M, seed=200 + M)
+    x, w, s = dev_tensor(inp["x"]), dev_tensor(inp["w"]), dev_tensor(inp["s"])
+    wt = m().moe_prepare_fp8_weights(w)
+    outs = {}
+    for tag in ("rows", "tiled"):
+        y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        if tag == "rows":
+            m().moe_fp8_linear(x, w, s, y=y)
+            m().moe_fp8_linear(x, w, s, y_f32=y32)
+        else:
+            m().moe_fp8_linear_tiled(x, wt, N, s, y=y)
+            m().moe_fp8_linear_tiled(x, wt, N, s, y_f32=y32)
+        torch.cuda.synchronize()
+        outs[tag] = (y.cpu().numpy(), y32.cpu().numpy().view(np.uint32))
+    assert np.array_equal(outs["rows"][0], outs["tiled"][0]), name
+    assert np.array_equal(outs["rows"][1], outs["tiled"][1]), name
