@@ -129,3 +129,50 @@ def test_graph_replay_of_the_fp32_slot_and_combine_modes():
         torch.cuda.synchronize()
         for key in ("ids", "slot", "sum", "out"):
             assert torch.equal(g_buf[key], e_buf[key]), f"replay {it}: {key} differs from eager"
+
+
+@pytest.mark.parametrize("N,K,M,tiled", [
+    (5120, 4096, 8, False),    # wo_b: K split into runs + the run reduce
+    (5120, 4096, 8, True),     # the same on the fragment-order weights
+    (16384, 1280, 5, True),    # wq_b: one run, no reduce
+])
+def test_graph_replay_of_the_dense_fp8_linear(N, K, M, tiled):
+    """moe_fp8_linear (or _tiled) captured once and replayed on changed activations: every replay equals an
+    eager call on the same inputs bit for bit, with eager work and a synchronization between replays."""
+    import synth
+    inp = synth.make_dense_inputs(N, K, M, seed=31)
+    w, s = dev_tensor(inp["w"]), dev_tensor(inp["s"])
+    wl = m().moe_prepare_fp8_weights(w) if tiled else w
+
+    def call(x, y, ws):
+        if tiled:
+            m().moe_fp8_linear_tiled(x, wl, N, s, y=y, ws=ws)
+        else:
+            m().moe_fp8_linear(x, wl, s, y=y, ws=ws)
+
+    xg, xe = dev_tensor(inp["x"]), dev_tensor(inp["x"])
+    yg, ye = (torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(2))
+    wsg, wse = m().fp8_linear_workspace(M, N, K), m().fp8_linear_workspace(M, N, K)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(xg, yg, wsg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(xg, yg, wsg)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for it in range(4):
+        xb = inp["x"][rng.permutation(M)].copy()
+        xb[rng.random(M) < 0.3] ^= np.uint16(0x8000)
+        xt = dev_tensor(xb)
+        xg.copy_(xt)
+        xe.copy_(xt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        call(xe, ye, wse)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye), f"replay {it}: dense output differs from eager"
