@@ -107,8 +107,9 @@ __global__ __launch_bounds__(256) void fp8_linear_stream(int M, int N, int K, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = lo + min(j + u, ns - 1);
-      RA[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes);
-      RB[u] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes + kHalf);
+      // weight bytes are read once per call: non-temporal loads
+      RA[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes));
+      RB[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc + (size_t)ks * kStepBytes + kHalf));
     }
   };
   load(PA, PB, 0);

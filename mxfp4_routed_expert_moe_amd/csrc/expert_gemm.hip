@@ -260,6 +260,9 @@ __device__ __forceinline__ void stage_run(uint8_t* lds, const uint8_t* src, int 
 
 template <int WF>
 struct StreamA;   // one 16-row x 128-K weight fragment of a lane
+// Weight bytes are read once per call, so the loads carry the non-temporal hint (streamed through the
+// caches without displacing other lines): decode_m8 GEMM1 83.4 -> 72.8 us, layer 142.8 -> 128.6 us, old
+// and new builds in alternating processes on one box.
 // `src` is the lane's first 16 bytes and KSTRIDE the bytes between consecutive 128-wide K steps: 64
 // along a stored row, 1024 between the fragments of the fragment-order copy. (A compile-time stride
 // keeps the prefetch addresses immediate offsets; computed at run time, the compiler waited for every
@@ -269,7 +272,7 @@ struct StreamA<W_MXFP4> {
   u32x4 d;
   template <int KSTRIDE>
   __device__ __forceinline__ void load(const uint8_t* src, int ks) {
-    d = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE);
+    d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ks * KSTRIDE));
   }
   __device__ __forceinline__ i32x8 frag() const {
     return i32x8{(int)d[0], (int)d[1], (int)d[2], (int)d[3], 0, 0, 0, 0};
@@ -281,8 +284,8 @@ struct StreamA<W_FP8_BLOCK32> {
   u32x4 d0, d1;
   template <int KSTRIDE>
   __device__ __forceinline__ void load(const uint8_t* src, int ks) {
-    d0 = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE);
-    d1 = *reinterpret_cast<const u32x4*>(src + ks * KSTRIDE + 64);
+    d0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ks * KSTRIDE));
+    d1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ks * KSTRIDE + 64));
   }
   __device__ __forceinline__ i32x8 frag() const {
     return i32x8{(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3], (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
