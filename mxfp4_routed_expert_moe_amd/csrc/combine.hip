@@ -37,7 +37,9 @@ __global__ __launch_bounds__(64) void combine_kernel(int H, int k, const int32_t
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       if (r < k) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(slot_out + ((size_t)t * k + order[r]) * H + c);
+        // each slot row is read once: non-temporal loads (M = 8192: 106 -> 90 us, alternating builds)
+        const u32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(slot_out + ((size_t)t * k + order[r]) * H + c));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[2 * i] = acc[2 * i] + bits_to_f32(v[i] << 16);
