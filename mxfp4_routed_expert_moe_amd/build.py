@@ -3,6 +3,7 @@
     python mxfp4_routed_expert_moe_amd/build.py
 
 Objects go to ``_build/`` at the repository root; the shared library is written next to this file.
+Also builds the test-only probe libraries under ``tests/csrc`` (never linked into libmoe.so).
 Always recompiles (cheap: a few seconds per source).
 """
 from __future__ import annotations
@@ -20,8 +21,12 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "combine.hip", "expand.hip",
-           "dense.hip", "moe_abi.cpp"]
+SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "expert_wide.hip", "combine.hip",
+           "expand.hip", "dense.hip", "moe_abi.cpp"]
+
+# test-only probes: source under tests/csrc -> tests/lib<name>.so
+PROBES = ["swiglu_probe"]
+TESTS = os.path.join(ROOT, "tests")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -34,8 +39,9 @@ FLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -45,18 +51,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    probes = [os.path.join(TESTS, "csrc", p + ".hip") for p in PROBES]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, SOURCES + probes))
+    _link(objs[: len(SOURCES)], LIB)
+    for name, obj in zip(PROBES, objs[len(SOURCES):]):
+        _link([obj], os.path.join(TESTS, f"lib{name}.so"))
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {len(PROBES)} test probe(s)")
     return LIB
 
 

@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void gather_act_scales_kernel(int P, int k, in
                                                                 const uint8_t* __restrict__ x_s, uint8_t* __restrict__ out) {
   const int pos = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
   if (pos >= P) return;
-  const int t = pairs[pos] / k;
+  const int t = pairs ? pairs[pos] / k : pos;
   reinterpret_cast<uint32_t*>(out)[(size_t)q * P + pos] =
       reinterpret_cast<const uint32_t*>(x_s + (size_t)t * q4 * 4)[q];
 }

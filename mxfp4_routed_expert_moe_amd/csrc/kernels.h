@@ -94,9 +94,15 @@ void launch_tile_map(int E, int max_tiles, const int32_t* offsets, int32_t* tile
 // (one stage's scales of 64 rows are 256 contiguous bytes instead of 64 strided dwords).
 void launch_scales_stage_major(int mats, int N, int K, const uint8_t* s, uint8_t* S, hipStream_t st);
 // Activation scales of the P = M*k sorted pairs, stage-major: out[K/128][P][4] from x_s[token][K/32],
-// token = pairs[pos] / k.
+// token = pairs[pos] / k (pairs == nullptr: token = pos, i.e. rows already in sorted order).
 void launch_gather_act_scales(int P, int k, int K, const int32_t* pairs, const uint8_t* x_s, uint8_t* out,
                               hipStream_t st);
+// MXFP4 weights in the fragment-order copy with stage-major scales of both operands (expert_wide.hip): the
+// 512 x 128 block tile, one wave per SIMD. Routed problems only.
+void launch_gemm1_wide(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
+                       const int32_t* info, hipStream_t s);
+void launch_gemm2_wide(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
+                       const int32_t* info, hipStream_t s);
 void launch_gemm1_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,
                        const int32_t* tile_r0, const int32_t* info, hipStream_t s);
 void launch_gemm2_mfma(WeightFormat f, const GemmProblem& p, int max_tiles, const int32_t* tile_e,

@@ -55,8 +55,9 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.sh_out = take(m * H * 2);
   // stage-major copies of the routed w1, w3 and w2 scales for the prefill-width GEMMs
   L.scales = take(m * k >= 32 * E ? 3 * E * I * H / 32 : 0);
-  // the activation scales of the sorted pairs, stage-major (prefill width)
-  L.xs_sm = take(m * k >= 32 * E ? m * k * H / 32 : 0);
+  // the activation scales of the sorted pairs, stage-major (prefill width: x_s gathered for GEMM1, or a
+  // caller's row-major h_s for GEMM2)
+  L.xs_sm = take(m * k >= 32 * E ? m * k * std::max(H, I) / 32 : 0);
   // the gate split into three bf16 planes for the matrix-core router (M > 64)
   L.gate_planes = take(m > (size_t)moe::kRouterSmallM ? 3 * E * H * 2 : 0);
   L.total = off;
@@ -139,6 +140,15 @@ inline bool routed_mfma(const moe_dims* d, int M, const moe_mxfp4_experts* packe
   return packed != nullptr && (int64_t)M * d->top_k >= 32 * (int64_t)d->num_experts;
 }
 inline bool shared_mfma(int M) { return M > 64; }
+// The 512 x 128 tile kernels (expert_wide.hip) serve the fragment-order MXFP4 copy at prefill width while every
+// operand they address stays below 2^31 bytes (32-bit buffer offsets); beyond that the register kernel of
+// expert_mfma.hip takes over.
+inline bool routed_wide(const moe_dims* d, int M, const moe_mxfp4_experts* packed) {
+  if (!routed_mfma(d, M, packed) || packed->tiled_weights == nullptr) return false;
+  const int64_t P = (int64_t)M * d->top_k, lim = int64_t(1) << 31;
+  return (int64_t)M * d->hidden < lim && P * d->inter < lim && P * d->hidden / 32 < lim &&
+         (int64_t)d->inter * d->hidden / 2 < lim;
+}
 
 struct TileMap {
   int max_tiles = 0;
@@ -214,11 +224,14 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
       p.sa = s1; p.sb = s3;
     }
     p.s_stage_major = 1;
-    if (tm.act_sm) {   // h stays in the workspace: both GEMMs take their activation scales stage-major
+    const bool wide = routed_wide(d, M, packed);
+    if (wide || tm.act_sm) {   // the activation scales of the sorted pairs, stage-major
       moe::launch_gather_act_scales(M * k, k, H, pairs, xs, tm.xs_sm, s);
-      p.act_s = tm.xs_sm; p.a_stage_major = 1; p.h_s_stage_major = 1;
+      p.act_s = tm.xs_sm; p.a_stage_major = 1;
     }
-    moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+    p.h_s_stage_major = tm.act_sm ? 1 : 0;   // h stays in the workspace: GEMM2 reads its scales stage-major
+    if (wide) moe::launch_gemm1_wide(p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+    else moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   }
   else if (packed) moe::launch_gemm1_stream(f, p, max_active, s);
   else moe::launch_gemm1_small(f, p, max_active, s);
@@ -260,7 +273,15 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
     }
     q.s_stage_major = 1;
     q.a_stage_major = tm.act_sm ? 1 : 0;
-    moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+    if (routed_wide(d, M, packed)) {
+      if (!tm.act_sm) {   // a caller's h_s [P, I/32] by sorted position: re-laid out stage-major first
+        moe::launch_gather_act_scales(M * k, 1, I, nullptr, hs, tm.xs_sm, s);
+        q.act_s = tm.xs_sm; q.a_stage_major = 1;
+      }
+      moe::launch_gemm2_wide(q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+    } else {
+      moe::launch_gemm2_mfma(f, q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
+    }
   }
   else if (packed) moe::launch_gemm2_stream(f, q, max_active, s);
   else moe::launch_gemm2_small(f, q, max_active, s);
@@ -301,6 +322,58 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
   q.out = out; q.out_f32 = out_f32;
   if (shared_mfma(M)) moe::launch_gemm2_mfma(moe::W_FP8_BLOCK32, q, 0, none.tile_e, none.tile_r0, none.info, s);
   else moe::launch_gemm2_stream(moe::W_FP8_BLOCK32, q, 1, s);
+}
+
+// Argument checks of moe_forward (everything except the workspace).
+moe_status check_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                         const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
+                         const moe_fp8_expert* shared, const uint16_t* out, const int32_t* ids_out,
+                         const float* rw_out, const uint16_t* shared_out) {
+  MOE_TRY(check_dims(dims, M));
+  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
+  if (shared != nullptr) MOE_TRY(check_shared(shared));
+  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
+  if ((ids_out && !al(ids_out, 4)) || (rw_out && !al(rw_out, 4)) || (shared_out && !al(shared_out, 16)))
+    return MOE_ERR_INVALID_ARG;
+  if (shared_out != nullptr && shared == nullptr) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// The whole layer on a validated workspace of ws_layout(dims, M).total bytes. No kernel relies on the
+// workspace's previous contents: every buffer is written before it is read within the call.
+void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
+                  const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
+                  uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws, hipStream_t s) {
+  const WsLayout L = ws_layout(dims, M);
+  int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
+  float* rw = rw_out ? rw_out : at<float>(ws, L.rw);
+  uint8_t* xq = at<uint8_t>(ws, L.x_q);
+  uint8_t* xs = at<uint8_t>(ws, L.x_s);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* pairs = at<int32_t>(ws, L.pairs);
+  int32_t* active = at<int32_t>(ws, L.active);
+  if (M <= moe::kRouterSmallM) {   // decode widths: logits + QDQ, then selection and permutation in one block
+    float* logits = at<float>(ws, L.logits);
+    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, nullptr, s);
+    moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
+                                     gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
+                                     at<int32_t>(ws, L.inv), active, s);
+  } else {
+    do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
+    moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
+                        at<int32_t>(ws, L.inv), active, s);
+  }
+  uint16_t* slot = at<uint16_t>(ws, L.slot);
+  do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
+                at<uint8_t>(ws, L.h_s), true, ws, s);
+  uint16_t* sh_out = nullptr;
+  if (shared != nullptr) {
+    sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
+    do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
+  }
+  moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
 }
 
 }  // namespace
@@ -434,45 +507,11 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                        const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
                        uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
                        size_t ws_bytes, void* stream) {
-  MOE_TRY(check_dims(dims, M));
-  if ((packed == nullptr) == (decoded == nullptr)) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_forward(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out));
   if (M == 0) return MOE_OK;
-  MOE_TRY(packed ? check_packed(packed) : check_decoded(decoded));
-  if (shared != nullptr) MOE_TRY(check_shared(shared));
-  if (!al(x, 16) || !al(gate_w, 16) || !al(gate_b, 4) || !al(out, 16)) return MOE_ERR_INVALID_ARG;
-  if ((ids_out && !al(ids_out, 4)) || (rw_out && !al(rw_out, 4)) || (shared_out && !al(shared_out, 16)))
-    return MOE_ERR_INVALID_ARG;
-  if (shared_out != nullptr && shared == nullptr) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const WsLayout L = ws_layout(dims, M);
-  int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
-  float* rw = rw_out ? rw_out : at<float>(ws, L.rw);
-  uint8_t* xq = at<uint8_t>(ws, L.x_q);
-  uint8_t* xs = at<uint8_t>(ws, L.x_s);
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* pairs = at<int32_t>(ws, L.pairs);
-  int32_t* active = at<int32_t>(ws, L.active);
-  if (M <= moe::kRouterSmallM) {   // decode widths: logits + QDQ, then selection and permutation in one block
-    float* logits = at<float>(ws, L.logits);
-    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, nullptr, s);
-    moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
-                                     gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
-                                     at<int32_t>(ws, L.inv), active, s);
-  } else {
-    do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
-    moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
-                        at<int32_t>(ws, L.inv), active, s);
-  }
-  uint16_t* slot = at<uint16_t>(ws, L.slot);
-  do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
-                at<uint8_t>(ws, L.h_s), true, ws, s);
-  uint16_t* sh_out = nullptr;
-  if (shared != nullptr) {
-    sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
-    do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
-  }
-  moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+  forward_impl(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out, ws,
+               static_cast<hipStream_t>(stream));
   return launched();
 }
 

@@ -101,22 +101,28 @@ def f32(v) -> np.ndarray:
     return np.asarray(v, dtype=np.float64).astype(np.float32)
 
 
+def _e2m1_byte_table() -> np.ndarray:
+    """[256, 2] fp64: the values of the low and the high nibble of every packed byte."""
+    b = np.arange(256)
+    return np.stack([e2m1_decode(b & 0xF), e2m1_decode(b >> 4)], axis=1)
+
+
+_E2M1_BYTE = _e2m1_byte_table()
+
+
 def decode_mxfp4(w: np.ndarray, s: np.ndarray) -> np.ndarray:
     """Packed MXFP4 matrix -> fp64 values.
 
     ``w`` uint8 [rows, cols/2] (low nibble = even column), ``s`` uint8 E8M0 [rows, cols/32].
-    Each value is ``e2m1(code) * 2^(b-127)``, exact (native-tensor page, section 2).
+    Each value is ``e2m1(code) * 2^(b-127)``, exact (native-tensor page, section 2). Byte j of a row
+    looks up its two values (low nibble first) in a table of all 256 bytes.
     """
     rows, half = w.shape
-    lo = e2m1_decode(w & 0xF)
-    hi = e2m1_decode(w >> 4)
-    vals = np.empty((rows, 2 * half), dtype=np.float64)
-    vals[:, 0::2] = lo
-    vals[:, 1::2] = hi
     scale = e8m0_decode(s)
     if scale.shape != (rows, 2 * half // 32):
         raise ValueError("MXFP4 scale shape mismatch")
-    return vals * np.repeat(scale, 32, axis=1)
+    vals = _E2M1_BYTE[w].reshape(rows, 2 * half // 32, 32)
+    return (vals * scale[:, :, None]).reshape(rows, 2 * half)
 
 
 def decode_fp8_blocks(w: np.ndarray, s: np.ndarray) -> np.ndarray:

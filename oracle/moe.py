@@ -118,11 +118,11 @@ def act_qdq(vals: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
 # ----------------------------------------------------------------------------------------------
 # expert FFN (section 2, "Expert"; section 4, math per (t, j))
 # ----------------------------------------------------------------------------------------------
-def swiglu(g: np.ndarray, u: np.ndarray, rw: np.ndarray | None) -> np.ndarray:
-    """h16 = bf16(rw * ((g / (1 + exp(-g))) * u)) with the clamps u in [-10, 10], g <= 10.
+def swiglu_f32(g: np.ndarray, u: np.ndarray, rw: np.ndarray | None) -> np.ndarray:
+    """The fp32 value h = rw * ((g / (1 + exp(-g))) * u) with the clamps u in [-10, 10], g <= 10.
 
     g and u are bf16 values; every operation is an fp32 operation (exp correctly rounded);
-    ``rw`` is None for the shared expert (no route weight). Returns bf16 values as fp64.
+    ``rw`` (one per row) is None for the shared expert (no route weight). Returns an fp32 array.
     """
     g32 = np.minimum(g, 10.0).astype(np.float32)
     u32 = np.clip(u, -10.0, 10.0).astype(np.float32)
@@ -133,7 +133,12 @@ def swiglu(g: np.ndarray, u: np.ndarray, rw: np.ndarray | None) -> np.ndarray:
     h = (sg * u32).astype(np.float32)
     if rw is not None:
         h = (np.asarray(rw, dtype=np.float32)[:, None] * h).astype(np.float32)
-    return F.bf16_rne(h.astype(np.float64))
+    return h
+
+
+def swiglu(g: np.ndarray, u: np.ndarray, rw: np.ndarray | None) -> np.ndarray:
+    """h16 = bf16(swiglu_f32(g, u, rw)) (RNE), returned as fp64 values."""
+    return F.bf16_rne(swiglu_f32(g, u, rw).astype(np.float64))
 
 
 def expert_ffn(xhat: np.ndarray, rw: np.ndarray | None, w1: np.ndarray, w3: np.ndarray,
@@ -152,16 +157,18 @@ def expert_ffn(xhat: np.ndarray, rw: np.ndarray | None, w1: np.ndarray, w3: np.n
 
 
 class ExpertWeights:
-    """Decoded weights of the routed experts, decoded lazily and cached per expert.
+    """Decoded weights of the routed experts, decoded lazily per expert.
 
     ``arm="packed"`` decodes MXFP4 straight to fp64; ``arm="decoded"`` first expands each matrix to
     bf16 storage (``uint16``), the decoded-BF16 arm's own weights, and computes from those.
+    ``cache=False`` keeps no expert after use (128 decoded experts of the full-size layer would take
+    36 GB of fp64).
     """
 
-    def __init__(self, inp: dict, arm: str = "packed"):
+    def __init__(self, inp: dict, arm: str = "packed", cache: bool = True):
         if arm not in ("packed", "decoded"):
             raise ValueError(arm)
-        self.inp, self.arm, self.cache = inp, arm, {}
+        self.inp, self.arm, self.cache, self.keep = inp, arm, {}, cache
 
     def expand_bf16(self, e: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
         """Expanded bf16 bit patterns of expert e: w1, w3 [I, H] and w2 [H, I] (exact)."""
@@ -178,6 +185,8 @@ class ExpertWeights:
                      F.decode_mxfp4(i["w2"][e], i["s2"][e]))
             else:
                 w = tuple(F.bf16_from_bits(b) for b in self.expand_bf16(e))
+            if not self.keep:
+                return w
             self.cache[e] = w
         return self.cache[e]
 
@@ -236,7 +245,7 @@ def moe_forward(inp: dict, cfg, tokens=None, ids=None, rw=None, arm: str = "pack
     use_ids = r["ids"] if ids is None else np.asarray(ids, dtype=np.int32)
     use_rw = r["rw"] if rw is None else np.asarray(rw, dtype=np.float32)
     xq, xs, xhat = act_qdq(F.bf16_from_bits(xb))
-    W = weights if weights is not None else ExpertWeights(inp, arm)
+    W = weights if weights is not None else ExpertWeights(inp, arm, cache=False)
     R, k = use_ids.shape
     H, I = cfg.H, cfg.I
     slot_y = np.zeros((R, k, H))

@@ -45,8 +45,19 @@ def bf16_host(t: torch.Tensor) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def forward(cfg, d: dict, decoded=None, with_shared=True, M=None):
-    """Run moe_forward; returns dict of host arrays (out, ids, rw, shared_out)."""
+def tiled_of(cfg, d: dict):
+    """The packed experts with the prepared stage-major scales and the fragment-order copy of the codes (the
+    layout the bench streams), with no row-major weight pointers."""
+    import mxfp4_routed_expert_moe_amd as m
+    pk = packed_of(d)
+    st = m.moe_prepare_mxfp4_scales(dims_of(cfg), pk)
+    tw = m.moe_prepare_mxfp4_weights(dims_of(cfg), pk)
+    return m.MXFP4Experts(None, d["s1"], None, d["s3"], None, d["s2"], stage_scales=st, tiled_weights=tw)
+
+
+def forward(cfg, d: dict, decoded=None, with_shared=True, M=None, packed=None):
+    """Run moe_forward; returns dict of host arrays (out, ids, rw, shared_out). packed: another form of the
+    routed experts (e.g. tiled_of) instead of the row-major one."""
     import mxfp4_routed_expert_moe_amd as m
     M = cfg.M if M is None else M
     dims = dims_of(cfg)
@@ -56,8 +67,8 @@ def forward(cfg, d: dict, decoded=None, with_shared=True, M=None):
     rw = torch.empty((M, cfg.k), dtype=torch.float32, device="cuda")
     sh = shared_of(d) if with_shared else None
     sh_out = torch.empty((M, cfg.H), dtype=torch.int16, device="cuda") if sh is not None else None
-    m.moe_forward(dims, d["x"][:M], d["gate_w"], d["gate_b"], None if decoded is not None else packed_of(d), decoded,
-                  sh, out, ids, rw, sh_out, ws)
+    pk = None if decoded is not None else (packed if packed is not None else packed_of(d))
+    m.moe_forward(dims, d["x"][:M], d["gate_w"], d["gate_b"], pk, decoded, sh, out, ids, rw, sh_out, ws)
     torch.cuda.synchronize()
     res = dict(out=bf16_host(out), ids=ids.cpu().numpy(), rw=rw.cpu().numpy(), out_bits=out.cpu().numpy())
     if sh_out is not None:

@@ -2,8 +2,9 @@
 
 Bars: integer/byte/index outputs bit-exact (ids except documented ties within 1e-6, permutation,
 QDQ codes and scales, expansion, combine given equal inputs); the layer output within
-max|err| <= 2e-2 * max|ref| and relative L2 <= 5e-3. Full-size configs compare sampled tokens that
-the oracle computes one by one.
+max|err| <= 2e-2 * max|ref| and relative L2 <= 5e-3 on every token of every workload; the QDQ'd h codes
+identical to the oracle's on more than 99.9 % of elements (the exactness test of the native-tensor page,
+section 4 "Kernel contract": only fp32 summation order may flip a bf16 rounding).
 """
 import numpy as np
 import pytest
@@ -14,11 +15,16 @@ from oracle import formats as F
 from oracle import moe as O
 
 from gpu_helpers import (assert_within, bf16_host, check_routing, dev_tensor, dims_of, forward, inputs,
-                         packed_of, shared_of, upload)
+                         packed_of, shared_of, tiled_of, upload)
 
 pytestmark = pytest.mark.gpu
 
 _cache = {}
+_oracle = {}
+
+# the page's exactness bar: identical bf16 roundings (here the QDQ'd h codes that follow them) on more than
+# 99.9 % of elements
+H_CODE_BAR = 0.999
 
 
 def cfg_inputs(cid, **over):
@@ -36,14 +42,25 @@ def m():
     return lib
 
 
-def sample_tokens(cfg, inp, n=8, seed=0):
-    rng = np.random.default_rng(seed)
-    picks = {0, cfg.M - 1}
-    if inp["hot_rows"].size:
-        picks.update(int(t) for t in inp["hot_rows"][:2])
-    while len(picks) < min(n, cfg.M):
-        picks.add(int(rng.integers(0, cfg.M)))
-    return np.array(sorted(picks))
+def oracle_full(cid):
+    """The oracle's whole layer on every token of a workload (at the prefill size about 3.5 TFLOP of fp64:
+    a minute or so on the host), kept for the tests of that workload."""
+    if cid not in _oracle:
+        _oracle.clear()
+        cfg, inp, _ = cfg_inputs(cid)
+        _oracle[cid] = O.moe_forward(inp, cfg)
+    return _oracle[cid]
+
+
+def conditioned_out(cfg, inp, ref, res, diff, part="out"):
+    """The oracle's output with the tie-flagged tokens whose GPU routing differs recomputed on the GPU's
+    routing (ids and route weights)."""
+    out = ref[part] if part == "out" else O.combine(ref["ids"], ref["slot_y"], None)
+    if diff.size:
+        out = out.copy()
+        c = O.moe_forward(inp, cfg, tokens=diff, ids=res["ids"][diff], rw=res["rw"][diff])
+        out[diff] = c["out"] if part == "out" else O.combine(c["ids"], c["slot_y"], None)
+    return out
 
 
 # ---------------------------------------------------------------------------------------------
@@ -78,10 +95,9 @@ def test_route_and_qdq(cid):
     ref = O.route(inp["x"], inp["gate_w"], inp["gate_b"], cfg.k, cfg.route_scale)
     diff = check_routing(ids.cpu().numpy(), rw.cpu().numpy(), ref, cfg)
     print(f"config {cfg.name}: {len(diff)} tie-flagged tokens route differently, {int(ref['tie'].sum())} flagged")
-    rows = np.arange(M) if M <= 2048 else sample_tokens(cfg, inp, 256)
-    codes, sb, _ = O.act_qdq(F.bf16_from_bits(inp["x"][rows]))
-    assert np.array_equal(xq.cpu().numpy()[rows], codes)
-    assert np.array_equal(xs.cpu().numpy()[rows], sb)
+    codes, sb, _ = O.act_qdq(F.bf16_from_bits(inp["x"]))
+    assert np.array_equal(xq.cpu().numpy(), codes)
+    assert np.array_equal(xs.cpu().numpy(), sb)
 
 
 def test_qdq_codes_exhaustive_over_bf16():
@@ -182,35 +198,108 @@ def test_expert_ffn_on_oracle_routing(cid):
     hq_g[pr] = hq.cpu().numpy()
     same = np.mean(hq_g.reshape(M, k, cfg.I) == ref["hq"])
     print(f"{cfg.name}: h codes identical on {same:.5f} of elements")
-    assert same >= 0.99
+    assert same > H_CODE_BAR
 
 
-def _check_forward(cfg, inp, d, decoded=None, n_sample=8):
+def _check_forward(cfg, inp, d, decoded=None, cid=None):
+    """moe_forward on every token against the oracle (tie-flagged tokens the GPU routes differently are
+    compared with the oracle on the GPU's routing). cid: a workload whose oracle run is kept."""
     res = forward(cfg, d, decoded=decoded)
-    toks = np.arange(cfg.M) if cfg.M <= 64 else sample_tokens(cfg, inp, n_sample)
-    full = O.route(inp["x"], inp["gate_w"], inp["gate_b"], cfg.k, cfg.route_scale)
-    diff = check_routing(res["ids"], res["rw"], full, cfg)
-    cond = np.intersect1d(toks, diff)
-    ref = O.moe_forward(inp, cfg, tokens=toks)
-    if cond.size:   # tie-flagged tokens routed differently: the oracle follows the GPU's routing there
-        refc = O.moe_forward(inp, cfg, tokens=toks, ids=np.where(np.isin(toks, cond)[:, None], res["ids"][toks], ref["ids"]),
-                             rw=np.where(np.isin(toks, cond)[:, None], res["rw"][toks], ref["rw"]))
-        ref = refc
-    mx, l2 = assert_within(res["out"][toks], ref["out"], f"{cfg.name} output")
-    print(f"{cfg.name}: max-err ratio {mx:.3g}, rel-L2 {l2:.3g} on {toks.size} tokens")
-    return res, ref, toks
+    ref = oracle_full(cid) if cid is not None else O.moe_forward(inp, cfg)
+    diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
+    out_ref = conditioned_out(cfg, inp, ref, res, diff)
+    mx, l2 = assert_within(res["out"], out_ref, f"{cfg.name} output")
+    print(f"{cfg.name}: max-err ratio {mx:.3g}, rel-L2 {l2:.3g} on all {cfg.M} tokens; "
+          f"{int(ref['route']['tie'].sum())} tie-flagged, {diff.size} routed differently: {diff.tolist()[:20]}")
+    return res, ref, diff
 
 
 @pytest.mark.parametrize("cid", [0, 1, 2, 3, 4])
 def test_forward_matches_oracle(cid):
+    """Every token of every workload against the oracle. At the prefill sizes (8192 and 2048 tokens) the
+    same oracle run also checks the expert outputs of every (expert, 64-row group), and at 8192 tokens the
+    decoded-BF16 arm on every token."""
     cfg, inp, d = cfg_inputs(cid)
-    res, ref, toks = _check_forward(cfg, inp, d)
+    res, ref, diff = _check_forward(cfg, inp, d, cid=cid)
     if cfg.shared:
-        # the shared expert's output dominates the sum: check both parts on their own
-        assert_within(res["shared_out"][toks], ref["shared_y"], "shared expert")
+        # the shared expert's output dominates the sum: check both parts on their own, on every token
+        assert_within(res["shared_out"], ref["shared_y"], "shared expert")
         routed = forward(cfg, d, with_shared=False)
-        ref_routed = O.combine(ref["ids"], ref["slot_y"], None)
-        assert_within(routed["out"][toks], ref_routed, "routed part")
+        assert np.array_equal(routed["ids"], res["ids"])
+        assert_within(routed["out"], conditioned_out(cfg, inp, ref, res, diff, part="routed"), "routed part")
+    if cfg.M >= 2048:
+        _expert_outputs_per_row_group(cid)
+        _tiled_weights_every_token(cfg, inp, d, res, ref)
+    if cfg.M == 8192:
+        _decoded_arm_every_token(cfg, inp, d, res, ref)
+
+
+def _tiled_weights_every_token(cfg, inp, d, res_s, ref):
+    """The same layer on the fragment-order weight copy with prepared scales (the prefill kernels of that
+    layout): every token within tolerance of the oracle, routing identical to the stored-layout run."""
+    res_t = forward(cfg, d, packed=tiled_of(cfg, d))
+    assert np.array_equal(res_t["ids"], res_s["ids"])
+    diff = check_routing(res_t["ids"], res_t["rw"], ref["route"], cfg)
+    mx, l2 = assert_within(res_t["out"], conditioned_out(cfg, inp, ref, res_t, diff), "fragment-order weights")
+    print(f"fragment-order weights (M={cfg.M}): max-err ratio {mx:.3g}, rel-L2 {l2:.3g} on every token; "
+          f"{np.mean(res_t['out_bits'] == res_s['out_bits']):.5f} of outputs bit-identical to the stored layout")
+
+
+def _decoded_arm_every_token(cfg, inp, d, res_p, ref):
+    """The decoded-BF16 arm at the prefill size: routing identical to the packed arm's, every token within
+    tolerance of the oracle and of the packed arm."""
+    dec = _decoded_of(cfg, d)
+    res_d = forward(cfg, d, decoded=dec)
+    del dec
+    torch.cuda.empty_cache()
+    assert np.array_equal(res_d["ids"], res_p["ids"])
+    diff = check_routing(res_d["ids"], res_d["rw"], ref["route"], cfg)
+    mx, l2 = assert_within(res_d["out"], conditioned_out(cfg, inp, ref, res_d, diff), "decoded arm")
+    assert_within(res_d["out"], res_p["out"], "decoded vs packed arm")
+    print(f"decoded arm (M={cfg.M}): max-err ratio {mx:.3g}, rel-L2 {l2:.3g} on every token; "
+          f"{np.mean(res_d['out_bits'] == res_p['out_bits']):.5f} of outputs bit-identical to the packed arm")
+
+
+def _expert_outputs_per_row_group(cid):
+    """The prefill-width expert FFN on the oracle's routing at full size: every expert's slot outputs,
+    64 sorted rows at a time (any row tile of the kernels is a union of such groups, the last group of an
+    expert is its ragged tail), within the tolerance of the oracle's; h codes identical on > 99.9 %."""
+    cfg, inp, d = cfg_inputs(cid)
+    ref = oracle_full(cid)
+    M, k, E, H = cfg.M, cfg.k, cfg.E, cfg.H
+    dims = dims_of(cfg)
+    ws = m().workspace(dims, M)
+    ids = torch.from_numpy(ref["ids"]).cuda()
+    rw = torch.from_numpy(ref["rw"]).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pairs = torch.empty(M * k, dtype=torch.int32, device="cuda")
+    active = torch.empty(E, dtype=torch.int32, device="cuda")
+    m().moe_permute(dims, ids, counts, offsets, pairs, None, active)
+    slot = torch.empty((M * k, H), dtype=torch.int16, device="cuda")
+    hq = torch.empty((M * k, cfg.I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((M * k, cfg.I // 32), dtype=torch.uint8, device="cuda")
+    m().moe_expert_ffn(dims, dev_tensor(ref["xq"]), dev_tensor(ref["xs"]), packed_of(d), None, rw, offsets, pairs,
+                       active, slot, hq, hs, ws)
+    torch.cuda.synchronize()
+    got = bf16_host(slot)                                   # rows = pair ids t * k + j
+    want = ref["slot_y"].reshape(M * k, H)
+    off = offsets.cpu().numpy()
+    pr = pairs.cpu().numpy()
+    worst = (0.0, 0.0)
+    groups = 0
+    for e in range(E):
+        for r0 in range(off[e], off[e + 1], 64):
+            rows = pr[r0: min(r0 + 64, off[e + 1])]
+            mx, l2 = assert_within(got[rows], want[rows], f"expert {e}, sorted rows {r0}..")
+            worst = (max(worst[0], mx), max(worst[1], l2))
+            groups += 1
+    hq_g = np.empty((M * k, cfg.I), dtype=np.uint8)
+    hq_g[pr] = hq.cpu().numpy()
+    same = np.mean(hq_g == ref["hq"].reshape(M * k, cfg.I))
+    print(f"{cfg.name}: {groups} (expert, 64-row) groups within tolerance, worst max-err ratio {worst[0]:.3g}, "
+          f"rel-L2 {worst[1]:.3g}; h codes identical on {same:.5f} of elements")
+    assert same > H_CODE_BAR
 
 
 def test_decoded_arm_equals_packed_arm_and_oracle():
@@ -283,11 +372,12 @@ MFMA_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["stored", "tiled"])
 @pytest.mark.parametrize("over", MFMA_CASES, ids=lambda o: "M{M}_H{H}_I{I}_E{E}_k{k}".format(**o))
-def test_prefill_path_matches_oracle_on_every_token(over):
+def test_prefill_path_matches_oracle_on_every_token(over, tiled):
     cfg, inp, d = cfg_inputs(0, **over)
     assert cfg.M * cfg.k >= 32 * cfg.E
-    res = forward(cfg, d)
+    res = forward(cfg, d, packed=tiled_of(cfg, d) if tiled else None)
     ref = O.moe_forward(inp, cfg)
     diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
     if diff.size:
@@ -326,7 +416,7 @@ def test_prefill_path_h_codes_on_oracle_routing():
     same = np.mean(hq_g.reshape(M, k, cfg.I) == ref["hq"])
     same_s = np.mean(hs_g.reshape(M, k, -1) == ref["hs"])
     print(f"MFMA path: h codes identical on {same:.5f}, h scales on {same_s:.5f} of elements")
-    assert same >= 0.99 and same_s >= 0.99
+    assert same > H_CODE_BAR and same_s > H_CODE_BAR
     assert_within(bf16_host(slot).reshape(M, k, cfg.H), ref["slot_y"], "slot outputs (MFMA path)")
 
 
@@ -393,26 +483,7 @@ def test_decoded_arm_on_prefill_sized_layer():
     q_d = _h_codes(cfg, d, xq, xs, ids, rw, decoded=dec)
     same = np.mean(q_p == q_d)
     print(f"decoded vs packed arm (M=1000): h codes identical on {same:.5f}")
-    assert same >= 0.99
-
-
-def test_decoded_arm_cross_checks_packed_arm_at_prefill_size():
-    """The M=8192 prefill layer through both arms: identical routing, outputs within tolerance of each
-    other everywhere and of the oracle on sampled tokens."""
-    cfg, inp, d = cfg_inputs(3)
-    dec = _decoded_of(cfg, d)
-    res_d = forward(cfg, d, decoded=dec)
-    del dec
-    torch.cuda.empty_cache()
-    res_p = forward(cfg, d)
-    assert np.array_equal(res_d["ids"], res_p["ids"])
-    assert_within(res_d["out"], res_p["out"], "decoded vs packed arm")
-    print(f"decoded vs packed arm (M=8192): {np.mean(res_d['out_bits'] == res_p['out_bits']):.5f} of outputs bit-identical")
-    toks = sample_tokens(cfg, inp, 4, seed=7)
-    full = O.route(inp["x"], inp["gate_w"], inp["gate_b"], cfg.k, cfg.route_scale)
-    check_routing(res_d["ids"], res_d["rw"], full, cfg)
-    ref = O.moe_forward(inp, cfg, tokens=toks, ids=res_d["ids"][toks], rw=res_d["rw"][toks])
-    assert_within(res_d["out"][toks], ref["out"], "decoded arm (sampled tokens)")
+    assert same > H_CODE_BAR
 
 
 def test_prefill_path_runs_are_bit_identical():
@@ -442,7 +513,7 @@ def test_decode_width_with_fp8_shared_expert(M):
 @pytest.mark.parametrize("M", [1, 2, 4, 5, 10, 15, 20, 32])
 def test_verifier_widths_full_size_layer(M):
     """The full-size layer (hidden 5120, 128 MXFP4 experts, intermediate 2304, top-6) at the speculative
-    verifier widths: routing bit-exact except documented ties, outputs within tolerance on sampled tokens."""
+    verifier widths: routing bit-exact except documented ties, outputs within tolerance on every token."""
     cfg, inp, d = cfg_inputs(2)
     c = synth.get_config(2, M=M)
     res = forward(c, d, M=M)
@@ -450,10 +521,9 @@ def test_verifier_widths_full_size_layer(M):
     sub["x"] = inp["x"][:M]
     full = O.route(sub["x"], inp["gate_w"], inp["gate_b"], c.k, c.route_scale)
     diff = check_routing(res["ids"], res["rw"], full, c)
-    toks = np.unique(np.array([0, M - 1, M // 2]))
-    ref = O.moe_forward(sub, c, tokens=toks, ids=res["ids"][toks] if diff.size else None,
-                        rw=res["rw"][toks] if diff.size else None)
-    assert_within(res["out"][toks], ref["out"], f"M={M}")
+    ref = O.moe_forward(sub, c, ids=res["ids"] if diff.size else None, rw=res["rw"] if diff.size else None)
+    mx, l2 = assert_within(res["out"], ref["out"], f"M={M}")
+    print(f"M={M}: every token within tolerance (max-err ratio {mx:.3g}, rel-L2 {l2:.3g})")
 
 
 def test_decode_path_is_batch_invariant():
