@@ -168,6 +168,23 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
                        uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. The same layer as moe_forward (same arguments
+ * minus ws / ws_bytes, same kernels, bit-identical results), with its workspace in a library-owned device
+ * array of MOE_NOALLOC_SCRATCH_BYTES per GPU (held from the first call on a device until the process
+ * ends). It calls no allocating routine.
+ * Limit: the call is refused with MOE_ERR_WORKSPACE (nothing enqueued) when moe_workspace_bytes(dims, M)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES; the full-size layer (E 128, H 5120, I 2304, k 6) fits up to M = 64 with
+ * or without the shared expert. The stream must belong to the current device (else MOE_ERR_INVALID_ARG).
+ * Every call on one GPU uses that GPU's one array, and nothing in it needs clearing between calls (each
+ * call writes every buffer before reading it); calls that overlap in time on one GPU (different streams or
+ * threads) race on it and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w,
+                               const float* gate_b, const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
+                               const moe_fp8_expert* shared, uint16_t* out, int32_t* ids_out, float* rw_out,
+                               uint16_t* shared_out, void* stream);
+
 /* ---- fp32 partial outputs for a tensor-parallel split of I (section 3 "combine modes"; section 4 "outputs",
  * modes SLOT and COMBINE). A rank holding I/G of every expert's w1/w3 rows and w2 inputs (dims.inter =
  * I/G; QDQ blocks never straddle the cut) produces fp32 partial sums; after an all-reduce of the

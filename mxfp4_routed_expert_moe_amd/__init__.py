@@ -22,7 +22,7 @@ __all__ = [
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
     "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
     "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights", "moe_fp8_tiled_weights_bytes",
-    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled",
+    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -84,6 +84,9 @@ lib.moe_combine.restype = _I32
 lib.moe_forward.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
                             ctypes.POINTER(_FP8), _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_forward.restype = _I32
+lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, _P, ctypes.POINTER(_MXFP4),
+                                    ctypes.POINTER(_BF16), ctypes.POINTER(_FP8), _P, _P, _P, _P, _P]
+lib.moe_forward_noalloc.restype = _I32
 lib.moe_expert_ffn_f32.argtypes = [ctypes.POINTER(_Dims), _I32, _P, _P, ctypes.POINTER(_MXFP4), ctypes.POINTER(_BF16),
                                    _P, _P, _P, _P, _P, _P, _SZ, _P]
 lib.moe_expert_ffn_f32.restype = _I32
@@ -334,6 +337,24 @@ def moe_forward(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, deco
                          _ptr(rw_out, torch.float32), _ptr(shared_out, _BF), _ptr(ws, torch.uint8),
                          0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "moe_forward")
+
+
+# size of the library-owned workspace of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES in moe.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_forward_noalloc(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, decoded: BF16Experts | None,
+                        shared: FP8Expert | None, out, ids_out=None, rw_out=None, shared_out=None, stream=None):
+    """moe_forward with the library's own per-GPU workspace (no ws argument; see moe.h for the limit)."""
+    M = x.shape[0]
+    pk = ctypes.byref(packed.c()) if packed is not None else None
+    dc = ctypes.byref(decoded.c()) if decoded is not None else None
+    sh = ctypes.byref(shared.c()) if shared is not None else None
+    st = lib.moe_forward_noalloc(ctypes.byref(dims.c()), M, _ptr(x, _BF), _ptr(gate_w, torch.float32),
+                                 _ptr(gate_b, torch.float32), pk, dc, sh, _ptr(out, _BF),
+                                 _ptr(ids_out, torch.int32), _ptr(rw_out, torch.float32), _ptr(shared_out, _BF),
+                                 _stream(stream))
+    _check(st, "moe_forward_noalloc")
 
 
 def moe_expand_mxfp4(w, s, out, stream=None):

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -13,6 +14,9 @@
 namespace {
 
 using moe::GemmProblem;
+
+// Size of the library-owned workspace of moe_forward_noalloc (per GPU).
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
 
 struct WsLayout {
   size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
@@ -324,7 +328,7 @@ void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, c
   else moe::launch_gemm2_stream(moe::W_FP8_BLOCK32, q, 1, s);
 }
 
-// Argument checks of moe_forward (everything except the workspace).
+// Argument checks of moe_forward and moe_forward_noalloc (everything except the workspace).
 moe_status check_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
                          const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
                          const moe_fp8_expert* shared, const uint16_t* out, const int32_t* ids_out,
@@ -374,6 +378,41 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
     do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
   }
   moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+}
+
+}  // namespace
+
+// ---- the library-owned workspace of moe_forward_noalloc ---------------------------------------------
+// One array per GPU the library runs on, held until the process ends. In host code the name `scratch`
+// only stands in for the symbol: its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array for work on stream s (NULL = the current device's
+// default stream). The stream must belong to the current device.
+moe_status scratch_for_stream(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return MOE_ERR_INVALID_ARG;
+    if (sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -512,6 +551,20 @@ moe_status moe_forward(const moe_dims* dims, int32_t M, const uint16_t* x, const
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   forward_impl(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out, ws,
                static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status moe_forward_noalloc(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w,
+                               const float* gate_b, const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded,
+                               const moe_fp8_expert* shared, uint16_t* out, int32_t* ids_out, float* rw_out,
+                               uint16_t* shared_out, void* stream) {
+  MOE_TRY(check_forward(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out));
+  if (M == 0) return MOE_OK;
+  if (ws_layout(dims, M).total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  MOE_TRY(scratch_for_stream(s, &ws));
+  forward_impl(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out, ws, s);
   return launched();
 }
 

@@ -134,6 +134,31 @@ def test_forward_refuses_before_launch(lib):
     assert _forward(lib, Dims(128, 5120, 2304, 0, 1.5), 8) == INVALID
 
 
+def test_forward_noalloc_refuses_before_launch(lib):
+    """moe_forward_noalloc validates like moe_forward and refuses a batch whose workspace exceeds its
+    library-owned array (MOE_NOALLOC_SCRATCH_BYTES), all before touching the device."""
+    f = lib.moe_forward_noalloc
+    f.restype = ctypes.c_int32
+    lib.moe_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    d = big()
+
+    def call(M, x=FAKE, out=FAKE, packed=True, decoded=False):
+        pk = ctypes.byref(Packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)) if packed else None
+        dc = ctypes.byref(Three(FAKE, FAKE, FAKE)) if decoded else None
+        return f(ctypes.byref(d), ctypes.c_int32(M), ctypes.c_void_p(x), ctypes.c_void_p(FAKE),
+                 ctypes.c_void_p(FAKE), pk, dc, None, ctypes.c_void_p(out), None, None, None, None)
+
+    assert call(0) == OK
+    assert call(-1) == INVALID
+    assert call(8, x=0) == INVALID
+    assert call(8, out=FAKE + 2) == INVALID
+    assert call(8, packed=False) == INVALID
+    assert call(8, decoded=True) == INVALID
+    assert lib.moe_workspace_bytes(ctypes.byref(d), 64) <= 16 << 20 < lib.moe_workspace_bytes(ctypes.byref(d), 256)
+    assert call(256) == WORKSPACE
+
+
 def test_component_calls_refuse_before_launch(lib):
     d = big()
     r = lib.moe_route(ctypes.byref(d), 8, None, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
