@@ -9,9 +9,13 @@ Inputs are resident in HBM before the timed region starts. The expert weights ex
 step i uses replica i mod R, so the 256 MB last-level cache cannot serve them from a previous step.
 
 Printed: one JSON line. ``value`` is tokens/s of the M=8 decode-width layer (hidden 5120, 128 MXFP4
-experts, intermediate 2304, top-6). ``roofline`` describes the dominant kernel, the grouped w1/w3 GEMM.
-``prefill`` holds the same figures for the M=8192 prefill layer. ``cpu_baseline`` is the CPU oracle timed
-on a bounded sample of the decode workload on this host's cores.
+experts, intermediate 2304, top-6) over the K timed steps. ``step_us`` holds the median, p10 and p90 of
+200 per-step HIP-event samples taken after a 0.5 s settle, ``telemetry`` the GPU clock, power and
+temperature polled meanwhile. ``roofline`` describes the dominant kernel, the grouped w1/w3 GEMM.
+``prefill`` (8192 tokens), ``batched_decode_m64`` and ``prefill_shared_skew_m2048`` (2048 tokens with the FP8
+shared expert and 8 hot experts) hold the same figures for the other workloads, each with its layer's
+fractions of the HBM and MFMA peaks. ``peaks`` are this GPU's measured streaming-read and scaled-MFMA
+rates. ``cpu_baseline`` is the CPU oracle timed on bounded samples on this host's cores (all, and one).
 """
 from __future__ import annotations
 
@@ -228,94 +232,208 @@ def measure_widths(L: Layer, widths, steps: int, warmup: int) -> dict:
     return res
 
 
-def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled: bool = True) -> dict:
+class Telemetry:
+    """Clock, power and temperature of the GPU, polled from amdsmi in a background thread while the layer
+    runs back to back (null fields where the library or a reading is unavailable)."""
+
+    def __init__(self, period_s: float = 0.01):
+        import threading
+
+        self.samples = []
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = None
+        self.handle = None
+        try:
+            import amdsmi
+            import torch
+
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            props = torch.cuda.get_device_properties(torch.cuda.current_device())
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)   # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+                    break
+        except Exception:   # amdsmi missing or not permitted: telemetry is reported as unavailable
+            self.handle = None
+
+    def _read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        def num(k):
+            v = m.get(k)
+            return v if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF) else None
+        gfx = num("current_gfxclk")
+        if gfx is None and isinstance(m.get("current_gfxclks"), list):
+            vals = [v for v in m["current_gfxclks"] if isinstance(v, int) and 0 < v < 0xFFFF]
+            gfx = sum(vals) / len(vals) if vals else None
+        return dict(gfx_mhz=gfx, mem_mhz=num("current_uclk"), power_w=num("current_socket_power") or
+                    num("average_socket_power"), hotspot_c=num("temperature_hotspot"))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        out = dict(samples=len(self.samples), period_ms=self.period * 1e3, source="amdsmi gpu metrics")
+        for k in ("gfx_mhz", "mem_mhz", "power_w", "hotspot_c"):
+            v = sorted(x[k] for x in self.samples if x.get(k) is not None)
+            out[k] = None if not v else dict(min=v[0], median=v[len(v) // 2], max=v[-1])
+        return out
+
+
+def _percentiles(us):
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return dict(samples=int(a.size), median=round(float(np.median(a)), 2), p10=round(float(np.percentile(a, 10)), 2),
+                p90=round(float(np.percentile(a, 90)), 2), min=round(float(a.min()), 2))
+
+
+def sample_steps(L: "Layer", n: int = 200, settle_s: float = 0.5) -> dict:
+    """After a 0.5 s settle, n steps each bracketed by its own pair of HIP events on the launch stream (the
+    weight replicas keep rotating): per-step microseconds as median, p10, p90."""
+    import torch
+    time.sleep(settle_s)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        L.step(i)
+        b.record()
+    torch.cuda.synchronize()
+    return _percentiles([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled: bool = True,
+            samples: int = 200) -> dict:
+    """One workload: the timed K-step loop (whole-job rate), 200 event samples, graph replay, the split
+    entry points' kernel times, GEMM1 back to back (roofline timing) and clock / power telemetry."""
     import torch
 
     L = Layer(cid, replicas, tiled)
     cfg = L.cfg
-    for i in range(warmup):
-        L.step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        L.step(warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / steps
-    D = L.distinct_experts()
+    tel = Telemetry()
+    if True:
+        for i in range(warmup):
+            L.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            L.step(warmup + i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / steps
+        D = L.distinct_experts()
+        ids_host = L.ids.cpu()
+        samp = sample_steps(L, samples)
 
-    # kernel-level times: events between the split entry points, on the stream they launch on
-    names = ["route", "permute", "gemm1", "gemm2", "shared", "combine"]
-    tot = [0.0] * len(names)
-    n_k = max(steps, 5)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_k)]
-    for i in range(warmup):
-        L.split_step(i, evs[0])
-    torch.cuda.synchronize()
-    for i in range(n_k):
-        L.split_step(warmup + i, evs[i])
-    torch.cuda.synchronize()
-    for ev in evs:
-        for j in range(len(names)):
-            tot[j] += ev[j].elapsed_time(ev[j + 1])
-    kern_us = {n: 1e3 * t / n_k for n, t in zip(names, tot)}
-    if L.shared is None:
-        kern_us.pop("shared")
-    # GEMM1's own duration for the roofline: back-to-back launches over the weight replicas (same routing;
-    # each launch streams another replica, so no launch finds its weights in cache), one event pair around
-    # the batch, so the per-call event and dispatch gaps of the split pass do not enter it
-    n_b = max(n_k, 2 * len(L.experts))
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    L.gemm1_only(0)
-    torch.cuda.synchronize()
-    b0.record()
-    for i in range(n_b):
-        L.gemm1_only(1 + i)
-    b1.record()
-    torch.cuda.synchronize()
-    gemm1_us = b0.elapsed_time(b1) * 1e3 / n_b
+        # kernel-level times: events between the split entry points, on the stream they launch on
+        names = ["route", "permute", "gemm1", "gemm2", "shared", "combine"]
+        tot = [0.0] * len(names)
+        n_k = max(min(steps, 50), 5)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_k)]
+        for i in range(warmup):
+            L.split_step(i, evs[0])
+        torch.cuda.synchronize()
+        for i in range(n_k):
+            L.split_step(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        for ev in evs:
+            for j in range(len(names)):
+                tot[j] += ev[j].elapsed_time(ev[j + 1])
+        kern_us = {n: 1e3 * t / n_k for n, t in zip(names, tot)}
+        if L.shared is None:
+            kern_us.pop("shared")
+        # GEMM1's own duration for the roofline: back-to-back launches over the weight replicas (same routing;
+        # each launch streams another replica, so no launch finds its weights in cache), one event pair around
+        # the batch, so the per-call event and dispatch gaps of the split pass do not enter it
+        n_b = max(n_k, 2 * len(L.experts))
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        L.gemm1_only(0)
+        torch.cuda.synchronize()
+        b0.record()
+        for i in range(n_b):
+            L.gemm1_only(1 + i)
+        b1.record()
+        torch.cuda.synchronize()
+        gemm1_us = b0.elapsed_time(b1) * 1e3 / n_b
+
+        # the same steps replayed from a HIP graph (one capture of R steps, one per weight replica): no host
+        # launch work between the kernels
+        R = len(L.experts)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                L.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(R):
+                L.step(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, steps // R)
+        g0, g1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(n_rep):
+            graph.replay()
+        g1e.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1e) / (n_rep * R)
+        # clock, power and temperature while the layer runs back to back (graph replays for about 0.4 s)
+        with tel:
+            t_end = time.perf_counter() + 0.4
+            while time.perf_counter() < t_end:
+                graph.replay()
+                torch.cuda.synchronize()
+        del graph
 
     w13_b, w2_b = _bytes_per_expert(cfg)
     f13, f2 = _flops_per_pair(cfg)
     P = cfg.M * cfg.k
     gemm1_bytes = D * w13_b + cfg.M * (cfg.H + cfg.H // 32) + P * (cfg.I + cfg.I // 32)
     gemm1_flops = P * f13
+    # the layer's algorithmic work: the touched experts' packed bytes (+ the fp32 gate, + the FP8 shared
+    # expert's bytes), and the flops of every (token, expert) assignment (+ the shared expert on every token)
     layer_bytes = D * (w13_b + w2_b) + cfg.E * cfg.H * 4
-    # the same steps replayed from a HIP graph (one capture of R steps, one per weight replica): no host
-    # launch work between the kernels
-    R = len(L.experts)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(R):
-            L.step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(R):
-            L.step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    n_rep = max(1, steps // R)
-    g0, g1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for _ in range(n_rep):
-        graph.replay()
-    g1e.record()
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1e) / (n_rep * R)
-    del graph
-
-    res = dict(workload=cfg.name, M=cfg.M, ms_per_step=ms, tokens_per_s=cfg.M / (ms * 1e-3), distinct_experts=D,
-               graph_ms_per_step=graph_ms,
-               kernel_us=kern_us, layer_weight_bytes=layer_bytes,
-               layer_hbm_frac=(layer_bytes / (ms * 1e-3)) / (HBM_PEAK_GBS * 1e9),
-               layer_tflops=(P * (f13 + f2)) / (ms * 1e-3) / 1e12, replicas=replicas, inputs_sha256=L.digest)
+    layer_flops = P * (f13 + f2)
+    if cfg.shared:
+        layer_bytes += 3 * cfg.I * cfg.H + 3 * (cfg.I // 32) * (cfg.H // 32)
+        layer_flops += cfg.M * (f13 + f2)
+    sec = ms * 1e-3
+    res = dict(workload=cfg.name, M=cfg.M, ms_per_step=ms, tokens_per_s=cfg.M / sec, distinct_experts=D,
+               graph_ms_per_step=graph_ms, step_us=samp, kernel_us=kern_us,
+               layer_algorithmic_bytes=layer_bytes, layer_algorithmic_flops=layer_flops,
+               layer_hbm_frac=(layer_bytes / sec) / (HBM_PEAK_GBS * 1e9),
+               layer_mfma_frac=(layer_flops / sec) / (MFMA_FP8_PEAK_TFLOPS * 1e12),
+               layer_tflops=layer_flops / sec / 1e12, replicas=replicas, weight_layout=L.weight_layout,
+               inputs_sha256=L.digest, telemetry=tel.summary(), ids=ids_host)
     g1 = gemm1_us * 1e-6
     timing = dict(avg_us_timing=f"HIP events around {n_b} back-to-back launches on the launch stream",
                   avg_us_per_call_events=round(kern_us["gemm1"], 2))
-    if cfg.M <= 64:
+    if cfg.M * cfg.k < 32 * cfg.E:   # decode width: the weight stream bounds GEMM1
         ach = gemm1_bytes / g1 / 1e9
         res["roofline"] = dict(kernel="expert_gemm1 (w1/w3 + SwiGLU + QDQ)", bound="hbm", achieved=round(ach, 1),
                                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
@@ -332,6 +450,62 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
     del L
     torch.cuda.empty_cache()
     return res
+
+
+def leg(r: dict) -> dict:
+    """The JSON object of one workload measured by measure() (value = tokens/s of the K-step loop)."""
+    return dict(workload=r["workload"], M=r["M"], value=round(r["tokens_per_s"], 1), unit="tokens/s",
+                ms_per_step=round(r["ms_per_step"], 5), step_us=r["step_us"],
+                graph_ms_per_step=round(r["graph_ms_per_step"], 5), distinct_experts=r["distinct_experts"],
+                kernel_us={k: round(v, 2) for k, v in r["kernel_us"].items()},
+                layer_hbm_frac=round(r["layer_hbm_frac"], 4), layer_mfma_frac=round(r["layer_mfma_frac"], 4),
+                layer_tflops=round(r["layer_tflops"], 1), roofline=r["roofline"], telemetry=r["telemetry"],
+                inputs_sha256=r["inputs_sha256"], weight_replicas=r["replicas"], weight_layout=r["weight_layout"])
+
+
+def measure_peaks() -> dict:
+    """This GPU's achievable peaks for the two rooflines (libpeaks.so, built with the library): a read of
+    2 GiB with 16-byte non-temporal loads, and dependency-free streams of the scaled 16x16x128 MFMA for the
+    three operand-format pairs, on every SIMD (512 blocks of 4 waves)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "libpeaks.so"))
+    lib.moe_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    sink = torch.empty(lib.moe_peak_stream_blocks(), dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    t = timed(lambda: lib.moe_peak_stream_read(buf.data_ptr(), n, sink.data_ptr(), st), 10)
+    out = dict(stream_read=dict(bytes=n, gbs=round(n / t / 1e9, 1), frac_of_8tbs=round(n / t / 8e12, 4),
+                                method="2 GiB read once per call, each wave a contiguous run of 1 KB loads "
+                                       "(16-byte non-temporal loads per lane), 10 calls"))
+    del buf
+    blocks, iters = 512, 4096
+    fsink = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
+    for name, fa, fb in (("e2m1_x_e4m3", 4, 0), ("e4m3_x_e4m3", 0, 0), ("e2m1_x_e2m1", 4, 4)):
+        t = timed(lambda: lib.moe_peak_mfma(fa, fb, blocks, iters, fsink.data_ptr(), st), 5)
+        flop = blocks * 4 * iters * 8 * 65536
+        out[f"mfma_{name}"] = dict(tflops=round(flop / t / 1e12, 1))
+    out["mfma_method"] = "v_mfma_scale_f32_16x16x128_f8f6f4, 8 independent accumulators per wave, 2 waves per SIMD"
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_dense(M: int = 8, reps: int = 40, pool_bytes: int = 1 << 30, tiled: bool = True) -> dict:
@@ -415,24 +589,66 @@ def calibrate_copy(gib: int = 1, reps: int = 5) -> dict:
     return dict(bytes_read=n, bytes_written=n, us=round(dt * 1e6, 1), gbs=round(2 * n / dt / 1e9, 1))
 
 
-def cpu_baseline(budget_tokens: int = 8) -> dict:
-    """The CPU oracle, as it stands, on the first token(s) of the decode workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(gpu_ids: dict | None = None) -> dict:
+    """The CPU oracle, as it stands, timed on bounded samples on this host:
+    - the decode workload's 8 tokens on all cores (the reported value), and 2 of them on one thread;
+    - the tiny layer (4 tokens) on all cores and on one thread;
+    - 4 tokens of the batched-decode workload on all cores.
+    Each run is the whole oracle layer for those tokens: router, QDQ, their experts decoded from MXFP4, fp64
+    dot products, SwiGLU, combine. Also reported: the oracle's routing of each measured workload, its
+    tie-flagged tokens (selection scores within 1e-6) and whether the GPU's ids differ there."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     import synth
     from oracle import moe as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: the BLAS pool size is unknown, report the host count
-        cores = os.cpu_count() or 1
-    cfg = synth.get_config(1)
-    inp = synth.make_inputs(cfg)
-    toks = list(range(budget_tokens))
-    t0 = time.perf_counter()
-    O.moe_forward(inp, cfg, tokens=toks)
-    dt = time.perf_counter() - t0
-    return dict(value=round(len(toks) / dt, 5), unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{len(toks)} token(s) of decode_m8 (router, QDQ, its {cfg.k} experts decoded from MXFP4, "
-                       f"fp64 dot products, combine); {dt:.1f} s")
+
+    pool = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+
+    inputs = {}
+
+    def run(cid, ntok, threads):
+        cfg = synth.get_config(cid)
+        if cid not in inputs:
+            inputs.clear()
+            inputs[cid] = synth.make_inputs(cfg)
+        inp = inputs[cid]
+        toks = list(range(ntok))
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            O.moe_forward(inp, cfg, tokens=toks)
+            dt = time.perf_counter() - t0
+        return dict(workload=cfg.name, tokens=ntok, threads=threads, seconds=round(dt, 2),
+                    tokens_per_s=round(ntok / dt, 4))
+
+    runs = [run(1, 8, pool), run(1, 2, 1), run(0, 4, pool), run(0, 4, 1), run(2, 4, pool)]
+    head = runs[0]
+    ties = {}
+    for name, ids in (gpu_ids or {}).items():
+        cfg = synth.get_config(WORKLOADS[name])
+        r = synth.make_router_inputs(cfg)
+        ref = O.route(r["x"], r["gate_w"], r["gate_b"], cfg.k, cfg.route_scale)
+        flagged = np.nonzero(ref["tie"])[0]
+        g = np.asarray(ids)
+        ties[name] = dict(flagged_tokens=[int(t) for t in flagged],
+                          gpu_ids_differ_at=[int(t) for t in flagged if not np.array_equal(g[t], ref["ids"][t])],
+                          untied_tokens_differing=int(np.sum(np.any(g != ref["ids"], axis=1) & ~ref["tie"])))
+    return dict(value=head["tokens_per_s"], unit="tokens/s", cores=head["threads"], kind="oracle",
+                sample=f"{head['tokens']} tokens of {head['workload']} (router, QDQ, their experts decoded from "
+                       f"MXFP4, fp64 dot products, combine); {head['seconds']} s",
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count(), runs=runs, routing_ties=ties)
 
 
 def main():
@@ -442,10 +658,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_m8", choices=sorted(WORKLOADS))
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the M=8192 measurement")
+    ap.add_argument("--samples", type=int, default=200, help="per-step HIP event samples after a 0.5 s settle")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the 64-token and 2048-token (shared expert, skewed routing) workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
     ap.add_argument("--no-widths", action="store_true", help="skip the verifier widths M = 1 .. 32")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the HBM-read and MFMA peak microbenchmarks")
     ap.add_argument("--stored-layout", action="store_true",
                     help="stream the weight codes (routed experts and the dense FP8 family) from their stored "
                          "row-major layout instead of the fragment-order copy made at load")
@@ -471,33 +691,50 @@ def main():
     if args.dense_only:
         print(json.dumps({"dense_fp8": measure_dense(tiled=not args.stored_layout)}), flush=True)
         return
-    widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
     tiled = not args.stored_layout
-    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths, tiled)
-    print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step "
-          f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f}), kernels {main_res['kernel_us']}",
-          file=sys.stderr, flush=True)
+    widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
+    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths, tiled, args.samples)
+    print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step, samples {main_res['step_us']}, "
+          f"kernels {main_res['kernel_us']}", file=sys.stderr, flush=True)
     if main_res.get("widths"):
         print("# widths: " + ", ".join(f"M={m}: {v['us']} us ({v['distinct_experts']} experts)"
                                        for m, v in main_res["widths"].items()), file=sys.stderr, flush=True)
-    prefill = None
-    if not args.no_prefill and args.workload != "prefill_m8192":
-        p = measure(3, max(3, args.steps // 10), max(1, args.warmup // 5), 2, tiled=tiled)
-        print(f"# {p['workload']}: {p['ms_per_step']:.3f} ms/step, kernels {p['kernel_us']}", file=sys.stderr,
-              flush=True)
-        prefill = dict(workload=p["workload"], value=round(p["tokens_per_s"], 1), unit="tokens/s",
-                       ms_per_step=round(p["ms_per_step"], 4), kernel_us={k: round(v, 1) for k, v in
-                                                                          p["kernel_us"].items()},
-                       graph_ms_per_step=round(p["graph_ms_per_step"], 4),
-                       layer_tflops=round(p["layer_tflops"], 1), roofline=p["roofline"])
+    gpu_ids = {main_res["workload"]: main_res.pop("ids").numpy()}
+    others = {}
+    plan = []
+    if not args.no_others:
+        plan.append(("batched_decode_m64", max(10, args.steps // 2), max(2, args.warmup // 2), args.replicas))
+    if not args.no_prefill:
+        plan.append(("prefill_m8192", max(20, args.steps // 5), max(4, args.warmup // 2), 2))
+    if not args.no_others:
+        plan.append(("prefill_shared_skew_m2048", max(20, args.steps // 5), max(4, args.warmup // 2), 2))
+    for name, st, wu, rep in plan:
+        if name == args.workload:
+            continue
+        r = measure(WORKLOADS[name], st, wu, rep, tiled=tiled, samples=args.samples)
+        gpu_ids[name] = r.pop("ids").numpy()
+        others[name] = leg(r)
+        print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, samples {r['step_us']}, kernels "
+              f"{ {k: round(v, 1) for k, v in r['kernel_us'].items()} }", file=sys.stderr, flush=True)
     dense = None
     if not args.no_dense:
-        dense = measure_dense(tiled=not args.stored_layout)
+        dense = measure_dense(tiled=tiled)
         summary = ", ".join(f"{k}: {v['us']} us" for k, v in dense["shapes"].items())
         print(f"# dense: {summary}", file=sys.stderr, flush=True)
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks()
+        print(f"# peaks: {peaks}", file=sys.stderr, flush=True)
+        for o in [main_res] + list(others.values()):
+            rf = o["roofline"]
+            if rf["bound"] == "hbm":
+                rf["measured_peak"] = peaks["stream_read"]["gbs"]
+            else:
+                rf["measured_peak"] = peaks["mfma_e2m1_x_e4m3"]["tflops"]
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / rf["measured_peak"], 4)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(gpu_ids)
     r = main_res
     line = {
         "metric": "MoE-layer tokens/s at M=8 and M=8192; % of HBM BW / MXFP4 MFMA roofline",
@@ -514,15 +751,21 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": r["workload"], "M": r["M"], "hidden": 5120, "experts": 128, "inter": 2304,
                    "top_k": 6, "distinct_experts": r["distinct_experts"], "weight_replicas": r["replicas"],
-                   "weight_layout": "stored row-major" if args.stored_layout else "fragment-order",
-                   "parallelism": "none (1 GPU)"},
+                   "weight_layout": r["weight_layout"], "parallelism": "none (1 GPU)"},
+        "step_us": r["step_us"],
         "graph_ms_per_step": round(r["graph_ms_per_step"], 5),
         "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()},
         "layer_hbm_frac": round(r["layer_hbm_frac"], 4),
+        "layer_algorithmic_bytes": r["layer_algorithmic_bytes"],
         "roofline": r["roofline"],
-        "prefill": prefill,
-        "verifier_widths": main_res.get("widths"),
+        "telemetry": r["telemetry"],
+        "inputs_sha256": r["inputs_sha256"],
+        "prefill": others.get("prefill_m8192"),
+        "batched_decode_m64": others.get("batched_decode_m64"),
+        "prefill_shared_skew_m2048": others.get("prefill_shared_skew_m2048"),
+        "verifier_widths": r.get("widths"),
         "dense_fp8": dense,
+        "peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

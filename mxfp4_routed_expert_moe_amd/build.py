@@ -26,6 +26,9 @@ SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "ex
 
 # test-only probes: source under tests/csrc -> tests/lib<name>.so
 PROBES = ["swiglu_probe"]
+# bench-only peak microbenchmarks: csrc/peaks.hip -> libpeaks.so next to libmoe.so
+PEAKS = "peaks.hip"
+PEAKS_LIB = os.path.join(PKG, "libpeaks.so")
 TESTS = os.path.join(ROOT, "tests")
 
 FLAGS = [
@@ -64,12 +67,14 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     probes = [os.path.join(TESTS, "csrc", p + ".hip") for p in PROBES]
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
-        objs = list(ex.map(_compile, SOURCES + probes))
-    _link(objs[: len(SOURCES)], LIB)
-    for name, obj in zip(PROBES, objs[len(SOURCES):]):
+        objs = list(ex.map(_compile, SOURCES + [PEAKS] + probes))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link([objs[n]], PEAKS_LIB)
+    for name, obj in zip(PROBES, objs[n + 1:]):
         _link([obj], os.path.join(TESTS, f"lib{name}.so"))
     if verbose:
-        print(f"built {LIB} and {len(PROBES)} test probe(s)")
+        print(f"built {LIB}, {PEAKS_LIB} and {len(PROBES)} test probe(s)")
     return LIB
 
 

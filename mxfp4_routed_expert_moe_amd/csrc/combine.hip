@@ -14,20 +14,24 @@ __global__ __launch_bounds__(64) void combine_kernel(int H, int k, const int32_t
                                                      uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
   // slots of this token sorted by ascending expert id (stable in slot order; k <= 8)
+  // (ids == nullptr: the rows are already in ascending-id order, as the decode-width layer writes them, and
+  // no id needs to be read)
   int order[8], key[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     order[j] = j;
-    key[j] = (j < k) ? ids[(size_t)t * k + j] : 0x7FFFFFFF;
+    key[j] = (j < k && ids) ? ids[(size_t)t * k + j] : 0x7FFFFFFF;
   }
+  if (ids) {
 #pragma unroll
-  for (int a = 1; a < 8; ++a)
+    for (int a = 1; a < 8; ++a)
 #pragma unroll
-    for (int b = a; b > 0; --b)
-      if (key[b] < key[b - 1]) {
-        const int tk = key[b]; key[b] = key[b - 1]; key[b - 1] = tk;
-        const int to = order[b]; order[b] = order[b - 1]; order[b - 1] = to;
-      }
+      for (int b = a; b > 0; --b)
+        if (key[b] < key[b - 1]) {
+          const int tk = key[b]; key[b] = key[b - 1]; key[b - 1] = tk;
+          const int to = order[b]; order[b] = order[b - 1]; order[b - 1] = to;
+        }
+  }
   {
     const int c = blockIdx.x * 512 + threadIdx.x * 8;   // H is a multiple of 128, so c + 8 <= H or c >= H
     if (c >= H) return;

@@ -32,9 +32,12 @@ void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* 
                     int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
 // M <= kRouterSmallM only: the router's selection (from the partial logit planes) and the counting sort in
 // one block; ids and rw equal launch_router_select_qdq's bit for bit.
+// out_rows (nullable) [M*k]: for each sorted position, the row t*k + r of its pair (t, j), r = the rank of
+// ids[t, j] among the token's k ids (ascending): slot rows written there are in ascending-id order per token.
 void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
                                  const float* gate_b, int32_t* ids, float* rw, int32_t* counts,
-                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
+                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, int32_t* out_rows,
+                                 hipStream_t s);
 
 // ---- expert GEMMs (expert_gemm.hip) --------------------------------------------------------
 enum WeightFormat { W_MXFP4 = 0, W_FP8_BLOCK32 = 1, W_BF16 = 2 };
@@ -61,6 +64,8 @@ struct GemmProblem {
   // outputs
   uint8_t* h_q; uint8_t* h_s;  // GEMM1: QDQ'd h codes [rows, N] and scales [rows, N/32]
   uint16_t* out;               // GEMM2: bf16 [*, N]; row = pair id (routed) or token (dense)
+  const int32_t* out_rows;     // GEMM2 (routed, decode-width kernels only): if set, the output row of each sorted
+                               // position instead of its pair id
   float* out_f32;              // GEMM2: if set, the unrounded fp32 sums [*, N] instead of out
   // MXFP4 scales in the stage-major copy made by launch_scales_stage_major (block-scaled MFMA kernels
   // only): [E][K/128][N][4] instead of [E][N][K/32]
@@ -134,6 +139,7 @@ void launch_fp8_linear_stream(int M, int N, int K, const uint16_t* x, const uint
                               const uint8_t* w, bool w_tiled, const uint8_t* s, float* part, uint16_t* y, float* y32,
                               hipStream_t st);
 
+// ids == nullptr: the token's k slot rows t*k .. t*k + k - 1 are already in ascending expert-id order.
 void launch_combine(int M, int H, int k, const int32_t* ids, const uint16_t* slot_out,
                     const uint16_t* shared_out, uint16_t* out, hipStream_t s);
 

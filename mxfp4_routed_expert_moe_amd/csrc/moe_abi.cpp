@@ -19,7 +19,7 @@ using moe::GemmProblem;
 constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
 
 struct WsLayout {
-  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
+  size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, out_rows, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
       sh_q, sh_s, sh_out, scales, xs_sm, gate_planes;
   size_t total;
 };
@@ -47,6 +47,7 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.offsets = take((E + 1) * 4);
   L.pairs = take(m * k * 4);
   L.inv = take(m * k * 4);
+  L.out_rows = take(m * k * 4);
   L.active = take(E * 4);
   L.tile_e = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
   L.tile_r0 = take((size_t)moe::mfma_max_tiles((int)(m * k), (int)E) * 4);
@@ -244,7 +245,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
 // GEMM2: H rows of w2 over I inputs; activation row = sorted position; output row = pair id.
 void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, const moe_mxfp4_experts* packed,
               const moe_bf16_experts* decoded, const int32_t* offsets, const int32_t* pairs, const int32_t* active,
-              uint16_t* slot, float* slot_f32, const TileMap& tm, hipStream_t s) {
+              uint16_t* slot, float* slot_f32, const TileMap& tm, hipStream_t s, const int32_t* out_rows = nullptr) {
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   const int max_active = (int)std::min<int64_t>(E, (int64_t)M * k);
   GemmProblem q{};
@@ -267,6 +268,8 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.N = H; q.K = I;
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot; q.out_f32 = slot_f32;
+  // (out_rows: the decode-width kernels only; the caller passes it only when no prefill-width kernel runs)
+  q.out_rows = routed_mfma(d, M, packed) ? nullptr : out_rows;
   if (routed_mfma(d, M, packed)) {
     if (packed->stage_scales != nullptr) {
       q.sa = packed->stage_scales + stage_scales_off(d, 2);
@@ -296,14 +299,15 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
 void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_mxfp4_experts* packed,
                    const moe_bf16_experts* decoded, const float* rw, const int32_t* offsets, const int32_t* pairs,
                    const int32_t* active, uint16_t* slot, float* slot_f32, uint8_t* hq, uint8_t* hs, bool h_internal,
-                   void* ws, hipStream_t s) {
+                   void* ws, hipStream_t s,
+                   const int32_t* out_rows = nullptr) {
   TileMap tm;
   if (routed_mfma(d, M, packed)) {
     tm = make_tile_map(d, M, offsets, ws, s);
     tm.act_sm = h_internal;
   }
   do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, tm, s);
-  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, slot_f32, tm, s);
+  do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, slot_f32, tm, s, out_rows);
 }
 
 void do_shared(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, const moe_fp8_expert* sh,
@@ -363,21 +367,24 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
     moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, nullptr, s);
     moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
                                      gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
-                                     at<int32_t>(ws, L.inv), active, s);
+                                     at<int32_t>(ws, L.inv), active, at<int32_t>(ws, L.out_rows), s);
   } else {
     do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
     moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
                         at<int32_t>(ws, L.inv), active, s);
   }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
+  // decode widths on the decode-width kernels: each token's slot rows are written in ascending expert-id order
+  // (rows from the selection kernel), so the combine reads no ids
+  const bool ranked = M <= moe::kRouterSmallM && !routed_mfma(dims, M, packed);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
-                at<uint8_t>(ws, L.h_s), true, ws, s);
+                at<uint8_t>(ws, L.h_s), true, ws, s, ranked ? at<int32_t>(ws, L.out_rows) : nullptr);
   uint16_t* sh_out = nullptr;
   if (shared != nullptr) {
     sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
     do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
   }
-  moe::launch_combine(M, dims->hidden, dims->top_k, ids, slot, sh_out, out, s);
+  moe::launch_combine(M, dims->hidden, dims->top_k, ranked ? nullptr : ids, slot, sh_out, out, s);
 }
 
 }  // namespace

@@ -1,0 +1,103 @@
+// Peak-rate microbenchmarks of the two rooflines the layer is measured against, on this GPU (a bench-only
+// library, libpeaks.so; not part of libmoe.so):
+//   moe_peak_stream_read - every byte of a device buffer read once with 16-byte non-temporal loads per lane,
+//                          the access the decode-width GEMMs make of the packed weights;
+//   moe_peak_mfma        - a dependency-free stream of v_mfma_scale_f32_16x16x128_f8f6f4 on every SIMD, for a
+//                          pair of operand formats (E2M1 x E4M3 is the pair of the routed experts).
+// Both write one value per wave or block so that no load or MFMA is removed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kReadBlocks = 4096;
+constexpr int kReadUnroll = 8;
+
+// Each wave reads a contiguous run of the buffer, 1 KB per load instruction (16 bytes per lane), kReadUnroll
+// loads in flight, as a decode GEMM wave streams its weight fragments; XOR-folded into one dword per block.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
+                                                          unsigned* __restrict__ sink) {
+  const size_t waves = (size_t)gridDim.x * 4;
+  const size_t wave = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const size_t per = (n16 / 64 + waves - 1) / waves;   // 1 KB pieces per wave
+  const size_t p0 = wave * per, p1 = min(p0 + per, n16 / 64);
+  unsigned x = 0;
+  size_t q = p0;
+  for (; q + kReadUnroll <= p1; q += kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + (q + u) * 64 + lane);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; q < p1; ++q) {
+    const u32x4 v = __builtin_nontemporal_load(buf + q * 64 + lane);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  __shared__ unsigned red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned r = 0;
+    for (int t = 0; t < 256; ++t) r ^= red[t];
+    sink[blockIdx.x] = r;
+  }
+}
+
+// iters x 8 MFMAs per wave on 8 independent accumulators. Operands are finite codes of each format (E4M3 and
+// E2M1 bytes 0x38 / 0x22 with small lane-dependent variation), scales 127 (1.0).
+template <int FA, int FB>
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int a8 = 0x38383838 ^ (lane & 3), a4 = 0x22222222 ^ ((lane & 1) << 1);
+  const int av = FA == 4 ? a4 : a8, bv = FB == 4 ? a4 : a8;
+  const i32x8 A = i32x8{av, av ^ 1, av, av ^ 1, av, av, av, av};
+  const i32x8 B = i32x8{bv, bv, bv ^ 1, bv, bv, bv ^ 1, bv, bv};
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, (float)j};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[j], FA, FB, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Number of dwords the sink of moe_peak_stream_read must hold.
+int moe_peak_stream_blocks(void) { return kReadBlocks; }
+
+// Reads `bytes` (a multiple of 1024) of the device buffer `buf` once; sink: device, moe_peak_stream_blocks()
+// dwords. Returns 0, -1 for a bad argument, -4 if the launch failed.
+int moe_peak_stream_read(const void* buf, size_t bytes, unsigned* sink, void* stream) {
+  if (!buf || !sink || bytes % 1024 != 0) return -1;
+  stream_read_kernel<<<dim3(kReadBlocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// `blocks` blocks of 4 waves, each wave issuing iters x 8 scaled 16x16x128 MFMAs of formats (fmt_a, fmt_b):
+// (4, 0) E2M1 x E4M3, (0, 0) E4M3 x E4M3 or (4, 4) E2M1 x E2M1. sink: device, 4 * blocks floats.
+// flop = blocks * 4 * iters * 8 * 65536. Returns 0, -1 for a bad argument, -4 if the launch failed.
+int moe_peak_mfma(int fmt_a, int fmt_b, int blocks, int iters, float* sink, void* stream) {
+  if (!sink || blocks <= 0 || iters <= 0) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt_a == 4 && fmt_b == 0) mfma_peak_kernel<4, 0><<<dim3(blocks), dim3(256), 0, s>>>(iters, sink);
+  else if (fmt_a == 0 && fmt_b == 0) mfma_peak_kernel<0, 0><<<dim3(blocks), dim3(256), 0, s>>>(iters, sink);
+  else if (fmt_a == 4 && fmt_b == 4) mfma_peak_kernel<4, 4><<<dim3(blocks), dim3(256), 0, s>>>(iters, sink);
+  else return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

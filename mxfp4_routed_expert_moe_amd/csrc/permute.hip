@@ -174,7 +174,7 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
     int M, int E, int k, float route_scale, int nparts, const float* __restrict__ logits,
     const float* __restrict__ gate_b, int32_t* __restrict__ ids, float* __restrict__ rw, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
-    int32_t* __restrict__ active) {
+    int32_t* __restrict__ active, int32_t* __restrict__ out_rows) {
   __shared__ int sid[kSmallPairs];
   __shared__ unsigned long long emask[256];
   __shared__ int soff[256];
@@ -225,6 +225,11 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
     const int pos = soff[v] + __popcll(emask[v] & ((1ull << t) - 1ull));
     pairs[pos] = tid;
     if (inv) inv[tid] = pos;
+    if (out_rows) {   // rank of this expert among the token's k (distinct) ids
+      int r = 0;
+      for (int j = 0; j < k; ++j) r += sid[t * k + j] < v ? 1 : 0;
+      out_rows[pos] = t * k + r;
+    }
   }
 }
 
@@ -238,14 +243,17 @@ void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* 
 
 void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
                                  const float* gate_b, int32_t* ids, float* rw, int32_t* counts,
-                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s) {
+                                 int32_t* offsets, int32_t* pairs, int32_t* inv, int32_t* active, int32_t* out_rows,
+                                 hipStream_t s) {
   const int parts = router_logit_parts(M, H);
   if (E <= 128)
     select_permute_small_kernel<2><<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, parts, logits, gate_b,
-                                                                         ids, rw, counts, offsets, pairs, inv, active);
+                                                                         ids, rw, counts, offsets, pairs, inv, active,
+                                                                         out_rows);
   else
     select_permute_small_kernel<4><<<dim3(1), dim3(kSmallPairs), 0, s>>>(M, E, k, route_scale, parts, logits, gate_b,
-                                                                         ids, rw, counts, offsets, pairs, inv, active);
+                                                                         ids, rw, counts, offsets, pairs, inv, active,
+                                                                         out_rows);
 }
 
 }  // namespace moe

@@ -27,7 +27,8 @@ from dataclasses import dataclass, field, asdict
 
 import numpy as np
 
-__all__ = ["LayerConfig", "CONFIGS", "get_config", "make_inputs", "make_tokens", "digest", "c4_hot_bias"]
+__all__ = ["LayerConfig", "CONFIGS", "get_config", "make_inputs", "make_router_inputs", "make_tokens", "digest",
+           "c4_hot_bias"]
 
 
 @dataclass(frozen=True)
@@ -122,10 +123,9 @@ def make_tokens(cfg: LayerConfig) -> np.ndarray:
     return _draw_tokens(np.random.Generator(np.random.PCG64(cfg.seed)), cfg)[0]
 
 
-def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
-    """Draw every input tensor of one layer invocation (numpy arrays, host memory)."""
-    rng = np.random.Generator(np.random.PCG64(cfg.seed))
-    M, H, E, I = cfg.M, cfg.H, cfg.E, cfg.I
+def _draw_router(rng: np.random.Generator, cfg: LayerConfig, hot_delta: float | None):
+    """The first draws of a layer: tokens, gate weight and bias (with the hot experts' increment)."""
+    E, H = cfg.E, cfg.H
     x, hot_rows = _draw_tokens(rng, cfg)
     gate_w = (rng.standard_normal((E, H)) * cfg.gate_std).astype(np.float32)
     gate_b = rng.uniform(-cfg.bias_half, cfg.bias_half, size=E).astype(np.float32)
@@ -134,6 +134,20 @@ def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
         hot_experts = np.sort(rng.choice(E, size=cfg.hot_experts, replace=False))
         delta = c4_hot_bias() if hot_delta is None else hot_delta
         gate_b[hot_experts] = (gate_b[hot_experts] + np.float32(delta)).astype(np.float32)
+    return x, hot_rows, gate_w, gate_b, hot_experts
+
+
+def make_router_inputs(cfg: LayerConfig) -> dict:
+    """Only x, gate_w and gate_b of make_inputs(cfg), drawn the same way (no expert weights)."""
+    x, _, gate_w, gate_b, _ = _draw_router(np.random.Generator(np.random.PCG64(cfg.seed)), cfg, None)
+    return dict(x=x, gate_w=gate_w, gate_b=gate_b)
+
+
+def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
+    """Draw every input tensor of one layer invocation (numpy arrays, host memory)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    M, H, E, I = cfg.M, cfg.H, cfg.E, cfg.I
+    x, hot_rows, gate_w, gate_b, hot_experts = _draw_router(rng, cfg, hot_delta)
     lo, hi = cfg.e8m0_lo, cfg.e8m0_hi + 1
     w1 = rng.integers(0, 256, size=(E, I, H // 2), dtype=np.uint8)
     s1 = rng.integers(lo, hi, size=(E, I, H // 32), dtype=np.uint8)

@@ -60,3 +60,12 @@ def test_prefill_hot_rows_and_skewed_routing():
     for k in ("sw1", "sw3", "sw2"):
         assert not np.any((i4[k] & 0x7F) == 0x7F)
     assert i4["ss1"].shape == (c4.I // 32, c4.H // 32) and i4["ss2"].shape == (c4.H // 32, c4.I // 32)
+
+
+def test_router_inputs_are_the_first_draws_of_make_inputs():
+    for cid in (0, 4):
+        cfg = synth.get_config(cid, M=16, H=256, E=16, I=128) if cid else synth.get_config(0)
+        full = synth.make_inputs(cfg)
+        r = synth.make_router_inputs(cfg)
+        for k in ("x", "gate_w", "gate_b"):
+            assert np.array_equal(r[k], full[k]), k
