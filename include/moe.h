@@ -2,7 +2,7 @@
  * moe.h - C ABI of the MI355X (gfx950) routed-MoE FFN layer library (libmoe.so).
  *
  * The layer is the DeepSeek-V4-Flash-style routed mixture-of-experts FFN defined on the
- * DeepSeek-V4.1-Flash native-tensor page ("Native 1017 DSpark draft on the NVLink pair"):
+ * page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)":
  *   section 2 "Official semantics" - quantized linear, activation QDQ, Gate, Expert, MoE;
  *   section 4 "Kernel contract"    - inputs, packed/expanded weight formats, per-(t, j) math, outputs.
  *
@@ -23,8 +23,13 @@
  * - M = 0 is a valid empty call (returns MOE_OK, enqueues nothing).
  *
  * Supported domain: 1 <= E <= 256, 1 <= k <= min(E, 8), H and I multiples of 128 and at most 8192, 0 <= M <= 2^24,
- * M * k <= 2^26, H * I <= 2^31. E8M0 scale bytes must be in 1..254 (255 is NaN; 0 is outside the
- * supported range); E4M3 weight bytes must be finite (not 0x7F/0xFF).
+ * M * k <= 2^26, H * I <= 2^31.
+ * H and I are inner dimensions of the matrix-core steps, which take 128 inputs at a time. An I that is a
+ * multiple of 32 only (e.g. a quarter of 2304) is refused; widen it to the next multiple of 128 with
+ * zero weight codes (w1 / w3 rows and w2 inputs of code 0, any valid scale): the padded rows give g = u =
+ * h = 0 and the padded w2 inputs multiply zero codes, so every output keeps its value.
+ * E8M0 scale bytes must be in 1..254 (255 is NaN; 0 is outside the supported range); E4M3 weight bytes
+ * must be finite (not 0x7F/0xFF).
  *
  * Data formats (section 2):
  * - bf16: uint16 bit pattern. fp32: float.
@@ -113,7 +118,12 @@ const char* moe_status_str(moe_status status);
 moe_status moe_route(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
                      int32_t* ids, float* rw, uint8_t* x_q, uint8_t* x_s, void* ws, size_t ws_bytes, void* stream);
 
-/* Token-to-expert permutation: a stable counting sort of the M*k pairs p = t*k + j by ids[p].
+/* Token-to-expert permutation: a stable counting sort of the M*k pairs p = t*k + j by ids[p]. The layer's
+ * math (section 2 "MoE") sums each token's k expert outputs; grouping the pairs by expert is how the
+ * expert GEMMs read each expert's packed weights once for all its rows: the expert sorter of the paper
+ * "DeepSeek-V4-Flash on AMD gfx90a" (section 7.1, rows of one expert gathered into blocks) and the
+ * (token, expert) emitter and the grouped route-direct chain screened on the page "DeepSeek V4 Flash
+ * REAP/XPU B70 Handoff". The order is stable, so the result does not depend on how the sort is scheduled.
  * counts int32 [E]; offsets int32 [E+1] (exclusive prefix sum, offsets[E] = number of valid pairs);
  * pairs int32 [M*k]: pair ids grouped by expert, ascending within an expert; inv int32 [M*k]
  * (nullable): position of each pair in `pairs`; active int32 [E]: experts with counts > 0 in

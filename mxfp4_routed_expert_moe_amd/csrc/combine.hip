@@ -1,4 +1,4 @@
-// Fixed-order combine of the routed experts (DeepSeek-V4.1-Flash native-tensor page, section 2
+// Fixed-order combine of the routed experts (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2
 // "MoE"): y = 0 in fp32; for the token's expert ids in ascending order, y += that expert's bf16
 // output (as fp32); then y += the shared expert's bf16 output; out = bf16(y). A block covers 512 columns
 // of one token (8 per thread); no atomics: the order of the adds is fixed by the ids, so the result is

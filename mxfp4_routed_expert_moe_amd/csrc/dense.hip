@@ -1,4 +1,4 @@
-// Dense FP8 linear of the method's projection family (DeepSeek-V4.1-Flash native-tensor page, section 4
+// Dense FP8 linear of the method's projection family (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 4
 // "Dense"): y = bf16(sum_k act_qdq(x) W) with W FP8 E4M3 [N, K] and one E8M0 scale per 32x32 block,
 // the same numerics as the shared expert's w2 (section 2 "Quantized linear").
 //
@@ -37,8 +37,6 @@ namespace {
 
 constexpr int kDenseInFlight = 1;       // K steps per weight register set (two sets take turns; 1 beat 2 and 4)
 constexpr int kDenseWaitVmLgkm0 = 0x7 << 4;   // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(0)
-constexpr int kDenseBlocks = 1024;      // blocks the K split aims for
-constexpr int kDenseMinSteps = 4;       // fewest K steps per run
 
 // copy of a run of nbytes (a multiple of UNIT) straight into LDS by one wave
 template <int UNIT>
@@ -199,26 +197,6 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(long long n4, int run
       *reinterpret_cast<u32x2*>(y + 4 * i) = u32x2{lo, hi};
     }
   }
-}
-
-DensePlan dense_plan(int M, int N, int K) {
-  DensePlan pl{};
-  const int nk = K / 128, cols = N / 64;
-  const int m16 = ((M + 15) / 16) * 16;
-  // LDS of one run: activation codes and scales of the M rows plus two weight-scale rows, within 48 KB
-  const int max_steps = std::max(1, 49152 / (m16 * 132 + 8));
-  int runs = std::max(1, std::min(nk, (kDenseBlocks + cols - 1) / cols));
-  // a block per CU already and the whole K fits in one run's LDS: no split, so no second launch
-  // (wq_b, 16384 x 1280 at M = 8: 8.4 us against 10.5 us in three runs)
-  if (cols >= 256 && nk <= max_steps) runs = 1;
-  int spr = (nk + runs - 1) / runs;
-  if (runs > 1) spr = std::min(std::max(spr, kDenseMinSteps), max_steps);
-  spr = std::min(spr, nk);
-  runs = (nk + spr - 1) / spr;
-  pl.runs = runs;
-  pl.steps_per_run = spr;
-  pl.lds = (size_t)M * spr * 132 + 2 * spr * 4;
-  return pl;
 }
 
 void launch_fp8_linear_stream(int M, int N, int K, const uint16_t* x, const uint8_t* xq, const uint8_t* xs,

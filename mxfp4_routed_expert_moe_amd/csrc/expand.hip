@@ -1,7 +1,7 @@
 // Expansion of packed MXFP4 matrices to bf16 (the decoded-BF16 arm's weights), and the fragment-order
 // copy of packed E2M1 codes that the routed GEMMs can stream from.
 //
-// Each value code * 2^(b-127) is exact in bf16 (DeepSeek-V4.1-Flash native-tensor page, section 2,
+// Each value code * 2^(b-127) is exact in bf16 (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2,
 // and section 4 "expanded weights ... values exactly code * 2^(b-127)"). A thread converts one
 // 32-value scale block: one 16-byte load of packed nibbles, 16 gfx950 conversions, four 16-byte stores.
 #include "kernels.h"

@@ -1,6 +1,6 @@
 // Expert GEMMs at decode width (few rows per expert) on gfx950.
 //
-// Math (DeepSeek-V4.1-Flash native-tensor page, section 4 "Kernel contract", per (t, j) with
+// Math (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 4 "Kernel contract", per (t, j) with
 // e = ids[t, j]): g = bf16(sum_k x w1), u = bf16(sum_k x w3), u = clamp(u, -10, 10), g = min(g, 10),
 // h = (g / (1 + exp(-g))) * u, h = rw * h, h16 = bf16(h), h_q = act_qdq(h16) per 32;
 // y = bf16(sum_k h_q w2). The shared expert (section 2 "Expert") is the same without rw.

@@ -1,7 +1,7 @@
 // Grouped expert GEMMs at prefill width (many rows per expert) on gfx950's block-scaled matrix cores, MXFP4
 // weights in the fragment-order copy: a 512 x 128 block tile with one wave per SIMD.
 //
-// Math (DeepSeek-V4.1-Flash native-tensor page, section 2 "Quantized linear" and section 4 "Kernel
+// Math (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Quantized linear" and section 4 "Kernel
 // contract"): per 32-wide K block the exact products of E4M3 activation codes and E2M1 weight codes are
 // summed, multiplied by the two E8M0 scales and accumulated in fp32; g and u are rounded to bf16, clamped,
 // h = rw * silu(g) * u in fp32, bf16, QDQ per 32 along I; y = bf16(h_hat w2^T). One

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dense_plan.h"
+
 namespace moe {
 
 // ---- router (route.hip) --------------------------------------------------------------------
@@ -15,11 +17,10 @@ namespace moe {
 constexpr int kRouterSmallM = 64;
 // fp32 logits of the raw bf16 activations against the fp32 gate weight [E, H], as
 // router_logit_parts(M, H) partial planes [parts, M, E] (summed in order by the select kernel).
-// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise); above, it first splits the gate into
-// gate_planes (3 * E * H bf16 of scratch).
+// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise).
 int router_logit_parts(int M, int H);
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, uint16_t* gate_planes, hipStream_t s);
+                          uint8_t* x_q, uint8_t* x_s, hipStream_t s);
 // sqrt(softplus) scores, biased top-k, normalised route weights; at M > kRouterSmallM also the
 // per-32 E4M3 QDQ of x.
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
@@ -124,14 +125,6 @@ void launch_combine_sum_f32(int M, int H, int k, const int32_t* ids, const float
 // ---- dense FP8 linear (dense.hip) ----------------------------------------------------------
 // Per-32 E4M3 QDQ of every row of x [M, K].
 void launch_qdq_rows(int M, int K, const uint16_t* x, uint8_t* xq, uint8_t* xs, hipStream_t s);
-// Decode-width plan: the K steps are split into runs of steps_per_run (one block column per run); lds =
-// dynamic LDS bytes per block. runs > 1 needs fp32 partials [runs, M, N].
-struct DensePlan {
-  int runs;
-  int steps_per_run;
-  size_t lds;
-};
-DensePlan dense_plan(int M, int N, int K);
 // y = bf16(x_hat W^T) (or fp32 into y32) for M <= 64: W FP8 [N, K] with E8M0 [N/32, K/32]; N % 64 == 0.
 // With x (bf16 [M, K]) the blocks QDQ their runs themselves and xq / xs are not read. w_tiled: w is the
 // fragment-order copy (launch_tile_mxfp4(1, N, 2 K, ...) of the row-major codes).

@@ -20,7 +20,7 @@ constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
 
 struct WsLayout {
   size_t logits, ids, rw, x_q, x_s, counts, offsets, pairs, inv, out_rows, active, tile_e, tile_r0, tile_info, h_q, h_s, slot,
-      sh_q, sh_s, sh_out, scales, xs_sm, gate_planes;
+      sh_q, sh_s, sh_out, scales, xs_sm;
   size_t total;
 };
 
@@ -63,8 +63,6 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   // the activation scales of the sorted pairs, stage-major (prefill width: x_s gathered for GEMM1, or a
   // caller's row-major h_s for GEMM2)
   L.xs_sm = take(m * k >= 32 * E ? m * k * std::max(H, I) / 32 : 0);
-  // the gate split into three bf16 planes for the matrix-core router (M > 64)
-  L.gate_planes = take(m > (size_t)moe::kRouterSmallM ? 3 * E * H * 2 : 0);
   L.total = off;
   return L;
 }
@@ -184,7 +182,7 @@ void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, cons
               float* rw, uint8_t* xq, uint8_t* xs, void* ws, hipStream_t s) {
   const WsLayout L = ws_layout(d, M);
   float* logits = at<float>(ws, L.logits);
-  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, xq, xs, at<uint16_t>(ws, L.gate_planes), s);
+  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, xq, xs, s);
   moe::launch_router_select_qdq(M, d->hidden, d->num_experts, d->top_k, d->route_scale, logits, gb, x, ids, rw, xq,
                                 xs, s);
 }
@@ -364,7 +362,7 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
   int32_t* active = at<int32_t>(ws, L.active);
   if (M <= moe::kRouterSmallM) {   // decode widths: logits + QDQ, then selection and permutation in one block
     float* logits = at<float>(ws, L.logits);
-    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, nullptr, s);
+    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, s);
     moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
                                      gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
                                      at<int32_t>(ws, L.inv), active, at<int32_t>(ws, L.out_rows), s);

@@ -1,6 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of the routed-MoE layer.
 //
-// Number formats follow the DeepSeek-V4.1-Flash native-tensor page, section 2 "Official semantics":
+// Number formats follow the page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Official semantics":
 // E2M1 nibbles (low nibble = even input), E8M0 scales 2^(b-127), FP8 E4M3 (OCP "e4m3fn"), bf16 with
 // round-to-nearest-even at every rounding point.
 #pragma once

@@ -1,7 +1,7 @@
 // Token-to-expert permutation: a stable counting sort of the M*k (token, slot) pairs by expert id.
 //
-// The expert GEMMs process the rows of one expert together (the grouped layout of the gfx90a paper,
-// section 7.1, and the route-direct chain of the Arc B70 page); the order inside an expert is
+// The expert GEMMs process the rows of one expert together (the grouped layout of the paper
+// "DeepSeek-V4-Flash on AMD gfx90a", section 7.1, and the route-direct chain of the page "DeepSeek V4 Flash REAP/XPU B70 Handoff"); the order inside an expert is
 // ascending pair id t*k + j, so results never depend on scheduling. No global atomics and no
 // in-kernel counter resets: block e counts with LDS atomics (integer, order-free) and compacts the
 // pairs of expert e with wave ballots.

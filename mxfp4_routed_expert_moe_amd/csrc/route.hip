@@ -1,6 +1,6 @@
 // Router of the routed-MoE layer on gfx950, and the per-32 E4M3 QDQ of its input rows.
 //
-// Gate (DeepSeek-V4.1-Flash native-tensor page, section 2 "Gate"): fp32 logits of the raw bf16 x
+// Gate (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Gate"): fp32 logits of the raw bf16 x
 // against the fp32 gate weight, scores sqrt(softplus(l)), top-k of scores + bias (the bias only
 // selects), gathered scores normalised by their sum + 1e-20 and scaled by the route scale.
 // Activation QDQ (same section, "Quantized linear"): per 32 inputs, E8M0 scale
@@ -87,31 +87,41 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
   }
 }
 
-// Larger M, on the bf16 matrix cores. The fp32 gate is first split into three bf16 planes whose sum is
-// exactly the gate (hi = the top 8 significand bits, mid = the next 8 of the remainder, lo = the rest,
+// Larger M, on the bf16 matrix cores. Each fp32 gate value is split into three bf16 parts whose sum is
+// exactly the value (hi = the top 8 significand bits, mid = the next 8 of the remainder, lo = the rest,
 // which has at most 8 bits): every product x * part is exact in fp32 (bf16 x bf16), so only the fp32
-// accumulation rounds, as in the vector path.
+// accumulation rounds, as in the vector path. The split is made in registers from the fp32 gate tile in
+// LDS, so the gate is read as it is stored and nothing is prepared or written per call.
 constexpr int kLargeParts = 4;
 
-__global__ __launch_bounds__(256) void gate_split_kernel(size_t n, const float* __restrict__ gate,
-                                                         uint16_t* __restrict__ planes) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    const float g = gate[i];
-    const uint32_t hi = __float_as_uint(g) & 0xFFFF0000u;
-    const float r1 = g - __uint_as_float(hi);                     // exact: the low 16 significand bits
-    const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
-    const float r2 = r1 - __uint_as_float(mid);                    // exact, at most 8 significant bits
-    planes[i] = uint16_t(hi >> 16);
-    planes[n + i] = uint16_t(mid >> 16);
-    planes[2 * n + i] = uint16_t(__float_as_uint(r2) >> 16);
+__device__ __forceinline__ void split_gate8(const f32x4& lo4, const f32x4& hi4, u32x4& p_hi, u32x4& p_mid,
+                                            u32x4& p_lo) {
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = i < 4 ? lo4[i] : hi4[i - 4];
+    const uint32_t vh = __float_as_uint(v) & 0xFFFF0000u;
+    const float r1 = v - __uint_as_float(vh);                       // exact: the low 16 significand bits
+    const uint32_t vm = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(vm);                      // exact, at most 8 significant bits
+    h[i] = vh >> 16;
+    m[i] = vm >> 16;
+    l[i] = __float_as_uint(r2) >> 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p_hi[i] = h[2 * i] | (h[2 * i + 1] << 16);
+    p_mid[i] = m[2 * i] | (m[2 * i + 1] << 16);
+    p_lo[i] = l[2 * i] | (l[2 * i + 1] << 16);
   }
 }
 
 // Block: 128 tokens x 128 experts over one quarter of H (the quarters are added in ascending order by the
-// select kernel). Per 32-wide K step, the block's x tile (128 rows x 64 B) and the three gate-plane tiles
-// (128 rows x 64 B each) stream into a three-stage LDS ring through direct global -> LDS copies, issued
-// two steps ahead; one copy per wave per tile (16 rows). The 16-byte chunks of each 64-byte LDS row are
-// XOR-swizzled (chunk ^ ((r ^ r >> 2) & 3)) so that the 16 rows of a fragment read distinct banks.
+// select kernel). Per 32-wide K step, the block's x tile (128 rows x 64 B, bf16) and fp32 gate tile
+// (128 rows x 128 B) stream into a three-stage LDS ring through direct global -> LDS copies, issued two
+// steps ahead; per wave one x copy (16 rows) and two gate copies (8 rows each). The 16-byte chunks of each
+// LDS row are XOR-swizzled (x: chunk ^ ((r ^ r >> 2) & 3); gate: chunk ^ (r & 7)) so that the 16 rows of a
+// fragment read distinct banks.
 // Wave w computes tokens 64 (w / 4) .. + 63 (four A tiles) x experts 32 (w % 4) .. + 31 (two B tiles):
 // per step and tile the hi, mid and lo products, in that order (v_mfma_f32_16x16x32_bf16: lane l
 // supplies row l % 16 of A and column l % 16 of B, inputs 8 (l / 16) .. + 7 of the step; the result
@@ -119,33 +129,37 @@ __global__ __launch_bounds__(256) void gate_split_kernel(size_t n, const float* 
 constexpr int kRtStages = 3;
 struct RouterStage {
   uint16_t x[128 * 32];
-  uint16_t g[3][128 * 32];
+  float g[128 * 32];
 };
 
 __device__ __forceinline__ int rt_key(int r) { return (r ^ (r >> 2)) & 3; }
 
 __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E, const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ gp, float* __restrict__ part) {
+                                                             const float* __restrict__ gate, float* __restrict__ part) {
   __shared__ __align__(16) RouterStage ring[kRtStages];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * 128, e0 = blockIdx.z * 128;
   const int hq = H / kLargeParts, hbeg = blockIdx.y * hq, nk = hq / 32;
-  const size_t plane = (size_t)E * H;
-  // copy sources: lane i of wave w fills LDS row 16 w + i / 4, physical chunk i % 4 (logical chunk
-  // (i % 4) ^ key); rows past M or E repeat the last row
+  // copy sources (rows past M or E repeat the last row): x - lane i of wave w fills LDS row 16 w + i / 4,
+  // physical chunk i % 4 (logical (i % 4) ^ key); gate copy c - lane i fills row 16 w + 8 c + i / 8,
+  // physical chunk i % 8 (logical (i % 8) ^ (row & 7))
   const int dr = 16 * wave + (lane >> 2), lc = (lane & 3) ^ rt_key(dr);
   const uint16_t* xsrc = x + (size_t)min(t0 + dr, M - 1) * H + hbeg + 8 * lc;
-  const uint16_t* gsrc = gp + (size_t)min(e0 + dr, E - 1) * H + hbeg + 8 * lc;
-  auto copy16 = [](const uint16_t* src, uint16_t* lds) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (__attribute__((address_space(3))) void*)lds, 16,
-                                     0, 0);
+  const float* gsrc[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int gr = 16 * wave + 8 * c + (lane >> 3), gc = (lane & 7) ^ (gr & 7);
+    gsrc[c] = gate + (size_t)min(e0 + gr, E - 1) * H + hbeg + 4 * gc;
+  }
+  auto copy16 = [](const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
   };
   auto issue = [&](int s) {
     RouterStage& st = ring[s % kRtStages];
     const int h = s * 32;
     copy16(xsrc + h, &st.x[16 * wave * 32]);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) copy16(gsrc + q * plane + h, &st.g[q][16 * wave * 32]);
+    for (int c = 0; c < 2; ++c) copy16(gsrc[c] + h, &st.g[(16 * wave + 8 * c) * 32]);
   };
   const int th = wave >> 2, eq = wave & 3;
   f32x4 acc[4][2];
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
   if (nk > 1) issue(1);
   for (int s = 0; s < nk; ++s) {
     // this wave's copies of step s have landed (those of step s + 1 may still be in flight), then meet
-    if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 1 < nk) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (s + 2 < nk) issue(s + 2);   // into the slot read at step s - 1: every wave is past it
     const RouterStage& st = ring[s % kRtStages];
@@ -170,8 +184,9 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int r = 32 * eq + 16 * b + r16;
-#pragma unroll
-      for (int q = 0; q < 3; ++q) B[b][q] = *reinterpret_cast<const u32x4*>(&st.g[q][r * 32 + 8 * (g ^ rt_key(r))]);
+      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&st.g[r * 32 + 4 * ((2 * g) ^ (r & 7))]);
+      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&st.g[r * 32 + 4 * ((2 * g + 1) ^ (r & 7))]);
+      split_gate8(lo4, hi4, B[b][0], B[b][1], B[b][2]);
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -217,13 +232,12 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
 int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : kLargeParts; }
 
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, uint16_t* gate_planes, hipStream_t s) {
+                          uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
   if (M <= kSmallM) {
     router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits,
                                                                                            x_q, x_s);
   } else {
-    gate_split_kernel<<<dim3(1024), dim3(256), 0, s>>>((size_t)E * H, gate_w, gate_planes);
-    router_logits_mfma<<<dim3((M + 127) / 128, kLargeParts, (E + 127) / 128), dim3(512), 0, s>>>(M, H, E, x, gate_planes,
+    router_logits_mfma<<<dim3((M + 127) / 128, kLargeParts, (E + 127) / 128), dim3(512), 0, s>>>(M, H, E, x, gate_w,
                                                                                                 logits);
   }
 }

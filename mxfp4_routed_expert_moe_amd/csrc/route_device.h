@@ -2,7 +2,7 @@
 // router kernels and the fused decode-width select + permute kernel, so that every path makes the same
 // decisions in the same fp32 order.
 //
-// Gate (DeepSeek-V4.1-Flash native-tensor page, section 2 "Gate"): scores sqrt(softplus(l)), top-k of
+// Gate (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Gate"): scores sqrt(softplus(l)), top-k of
 // scores + bias (the bias only selects), the chosen scores normalised by their sum + 1e-20 and scaled
 // by the route scale. Activation QDQ (same section, "Quantized linear"): per 32 inputs, E8M0 scale
 // 2^ceil(log2(max(amax, 1e-4) / 448)) and E4M3 codes.

@@ -14,9 +14,9 @@ Modules
 ``exact``    an independent pure-Python brute force (integer arithmetic) of the same layer for tiny
              shapes, used to pin ``moe``.
 
-Every function cites the passage it follows: the native-tensor page of the DeepSeek-V4.1-Flash draft
-("Native 1017 DSpark draft on the NVLink pair"), section 2 "Official semantics" and section 4 "Kernel
-contract"; the gfx90a paper ("DeepSeek-V4-Flash on AMD gfx90a"), section 6.1 for the E2M1 integer map.
+Every function cites the passage it follows: the page
+"Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Official semantics" and section 4 "Kernel
+contract"; the paper "DeepSeek-V4-Flash on AMD gfx90a", section 6.1 for the E2M1 integer map.
 
 Parity status: every function here is pinned by tests under ``tests/test_oracle_*.py`` (see each
 function's docstring for its pin). The end-to-end layer at full size is pinned only through the

@@ -2,7 +2,7 @@
 experts about half of all assignments (test infrastructure; calls only the oracle's router).
 
 The generator adds this delta to the drawn selection bias of the hot experts. The bias only selects
-experts (native-tensor page, section 2 "Gate"), so the delta shifts routing without touching any
+experts ("Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Gate"), so the delta shifts routing without touching any
 route weight. Bisection on delta until the hot share of the M*k assignments is within 0.5 +- 0.01.
 
     python -m oracle.calibrate_skew

@@ -2,7 +2,7 @@
 
 Test infrastructure only. It exists to pin ``oracle.moe`` and shares none of its code:
 
-* FP4 values come from the gfx90a paper's integer map (section 6.1: E2M1 times two is one of
+* FP4 values come from the integer map of the paper "DeepSeek-V4-Flash on AMD gfx90a" (section 6.1: E2M1 times two is one of
   0, +-1, +-2, +-3, +-4, +-6, +-8, +-12), not from the E2M1 table in ``oracle.formats``;
 * E4M3 values come from the OCP bit fields as integers times 2^-9, and E4M3 encoding is a nearest
   search over all codes rather than arithmetic rounding;
@@ -20,7 +20,7 @@ import struct
 
 EXP0 = 400  # values are held as integers times 2^-EXP0
 
-_FP4_X2 = [0, 1, 2, 3, 4, 6, 8, 12]   # gfx90a paper, section 6.1
+_FP4_X2 = [0, 1, 2, 3, 4, 6, 8, 12]   # "DeepSeek-V4-Flash on AMD gfx90a", section 6.1
 
 
 def fp4_int(nib: int) -> tuple[int, int]:

@@ -1,6 +1,6 @@
 """Exact number formats of the layer (oracle side; test infrastructure only).
 
-Definitions (native-tensor page, section 2 "Official semantics"):
+Definitions ("Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Official semantics"):
 
 * E2M1 (FP4): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, bit 3 is the sign (0b1000 is -0).
   Packed: byte j of a row holds input 2j in the low nibble and input 2j+1 in the high nibble.
@@ -114,7 +114,7 @@ def decode_mxfp4(w: np.ndarray, s: np.ndarray) -> np.ndarray:
     """Packed MXFP4 matrix -> fp64 values.
 
     ``w`` uint8 [rows, cols/2] (low nibble = even column), ``s`` uint8 E8M0 [rows, cols/32].
-    Each value is ``e2m1(code) * 2^(b-127)``, exact (native-tensor page, section 2). Byte j of a row
+    Each value is ``e2m1(code) * 2^(b-127)``, exact ("Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2). Byte j of a row
     looks up its two values (low nibble first) in a table of all 256 bytes.
     """
     rows, half = w.shape
@@ -128,7 +128,7 @@ def decode_mxfp4(w: np.ndarray, s: np.ndarray) -> np.ndarray:
 def decode_fp8_blocks(w: np.ndarray, s: np.ndarray) -> np.ndarray:
     """FP8 E4M3 matrix with one E8M0 per 32x32 block -> fp64 values.
 
-    ``w`` uint8 [rows, cols], ``s`` uint8 [ceil(rows/32), ceil(cols/32)] (native-tensor page, section 2).
+    ``w`` uint8 [rows, cols], ``s`` uint8 [ceil(rows/32), ceil(cols/32)] ("Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2).
     """
     rows, cols = w.shape
     scale = e8m0_decode(s)

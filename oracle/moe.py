@@ -1,7 +1,7 @@
 """The routed-MoE FFN layer, step by step, on the CPU (test infrastructure only).
 
-Follows the native-tensor page of the DeepSeek-V4.1-Flash draft ("Native 1017 DSpark draft on the
-NVLink pair"): section 2 "Official semantics" (quantized linear, activation QDQ, gate, expert, MoE)
+Follows the page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)":
+section 2 "Official semantics" (quantized linear, activation QDQ, gate, expert, MoE)
 and section 4 "Kernel contract" (the per-(token, slot) math of the routed expert).
 
 Precision: every linear output is the exact dot product of exactly decoded values, rounded once to

@@ -3,7 +3,7 @@
 This module only draws random numbers and arranges them in the storage formats the layer consumes.
 It holds none of the layer's arithmetic: no decoding of the formats, no quantisation, no routing.
 
-Storage formats (DeepSeek-V4.1-Flash native-tensor page, section 2 "Official semantics" and
+Storage formats (page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)", section 2 "Official semantics" and
 section 4 "Kernel contract"):
 
 * activations ``x``: bf16 stored as ``uint16`` bit patterns, shape [M, H];
@@ -28,7 +28,7 @@ from dataclasses import dataclass, field, asdict
 import numpy as np
 
 __all__ = ["LayerConfig", "CONFIGS", "get_config", "make_inputs", "make_router_inputs", "make_tokens", "digest",
-           "c4_hot_bias"]
+           "c4_hot_bias", "pad_inter"]
 
 
 @dataclass(frozen=True)
@@ -167,7 +167,31 @@ def make_inputs(cfg: LayerConfig, hot_delta: float | None = None) -> dict:
     return out
 
 
-# The dense FP8 projection family of the native-tensor page (section 4 "Dense"), N x K per rank.
+def pad_inter(inp: dict, I: int, I_pad: int) -> dict:
+    """The layer's weights with the intermediate width I (a multiple of 32) widened to I_pad by zero codes:
+    w1 / w3 (and the shared sw1 / sw3) gain rows of code 0, w2 (and sw2) input columns of code 0; the new
+    scale bytes are 127 (1.0). Layout only: the padded rows give g = u = 0, so h = 0, whose QDQ codes are 0,
+    and the padded w2 inputs are 0, so every output is the same value as with width I."""
+    assert I % 32 == 0 and I_pad >= I and I_pad % 32 == 0
+    n = I_pad - I
+    out = dict(inp)
+
+    def rows(a, cnt, axis, fill):
+        shape = list(a.shape)
+        shape[axis] = cnt
+        return np.concatenate([a, np.full(shape, fill, dtype=a.dtype)], axis=axis)
+
+    out["w1"], out["w3"] = rows(inp["w1"], n, 1, 0), rows(inp["w3"], n, 1, 0)
+    out["s1"], out["s3"] = rows(inp["s1"], n, 1, 127), rows(inp["s3"], n, 1, 127)
+    out["w2"], out["s2"] = rows(inp["w2"], n // 2, 2, 0), rows(inp["s2"], n // 32, 2, 127)
+    if "sw1" in inp:
+        out["sw1"], out["sw3"] = rows(inp["sw1"], n, 0, 0), rows(inp["sw3"], n, 0, 0)
+        out["ss1"], out["ss3"] = rows(inp["ss1"], n // 32, 0, 127), rows(inp["ss3"], n // 32, 0, 127)
+        out["sw2"], out["ss2"] = rows(inp["sw2"], n, 1, 0), rows(inp["ss2"], n // 32, 1, 127)
+    return out
+
+
+# The dense FP8 projection family of the page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)" (section 4 "Dense"), N x K per rank.
 DENSE_SHAPES = {
     "wq_a": (1280, 5120),
     "wkv": (512, 5120),

@@ -253,3 +253,31 @@ def test_dense_fp8_tiled_calls_refuse_before_launch(lib):
     assert lin(8, 1280, 5120, x, w, s, y, y, ws, 1 << 30, None) == INVALID           # both outputs
     assert lin(8, 1280, 5120, x, w, s, y, None, ws, 16, None) == WORKSPACE
     assert lin(0, 1280, 5120, x, w, s, y, None, ws, 0, None) == OK                   # empty batch: nothing to do
+
+
+def test_dense_plan_fits_lds_over_admitted_shapes(tmp_path):
+    """The decode-width dense linear's launch plan (csrc/dense_plan.h), built with the host compiler and run
+    over every admitted M <= 64 shape: dynamic LDS within the budget and every K step in exactly one run.
+    N = 65536 with K = 5120 at M = 64 was the shape where the block-count rule alone asked for 338 KB."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = tmp_path / "dense_plan_check"
+    src = os.path.join(ROOT, "tests", "csrc", "dense_plan_check.cpp")
+    inc = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc")
+    subprocess.run([cxx, "-O2", "-std=c++17", "-I", inc, src, "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    print(r.stdout.strip())
+
+
+def test_dense_workspace_holds_partials_of_split_plans(lib):
+    """Where the LDS cap splits K although N alone fills the chip, the workspace grows by the fp32 partials."""
+    lib.moe_fp8_linear_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_fp8_linear_workspace_bytes.argtypes = [ctypes.c_int32] * 3
+    M, N, K = 64, 65536, 5120
+    ws = lib.moe_fp8_linear_workspace_bytes(M, N, K)
+    # 48 KB / (64 * 132 + 8) = 5 steps per run -> 8 runs of the 40 steps
+    assert ws >= 8 * M * N * 4 + M * K + M * K // 32

@@ -3,7 +3,7 @@
 Bars: integer/byte/index outputs bit-exact (ids except documented ties within 1e-6, permutation,
 QDQ codes and scales, expansion, combine given equal inputs); the layer output within
 max|err| <= 2e-2 * max|ref| and relative L2 <= 5e-3 on every token of every workload; the QDQ'd h codes
-identical to the oracle's on more than 99.9 % of elements (the exactness test of the native-tensor page,
+identical to the oracle's on more than 99.9 % of elements (the exactness test of the page "Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)",
 section 4 "Kernel contract": only fp32 summation order may flip a bf16 rounding).
 """
 import numpy as np

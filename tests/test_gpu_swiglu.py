@@ -1,6 +1,6 @@
 """The device SwiGLU (the GEMM1 epilogue's fp32 chain in moe_device.h) against the oracle's.
 
-The page's expert computes h = rw * silu(g) * u in fp32 with a full-precision exp (native-tensor page,
+The page's expert computes h = rw * silu(g) * u in fp32 with a full-precision exp ("Native 1017 DSpark draft on the NVLink pair (N1-NATIVE)",
 section 4 "Kernel contract", math per (t, j)). The oracle evaluates that chain with a correctly rounded
 exp and IEEE division. The device evaluates exp as 2^(x log2 e) on the hardware base-2 exponential with a
 two-part log2 e, and the division as a hardware reciprocal plus one FMA correction. This test runs the

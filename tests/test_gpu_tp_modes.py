@@ -160,3 +160,42 @@ def test_two_rank_split_of_inter_meets_the_layer_tolerance(over):
     m().moe_combine_official_f32(r["dims"], r["ids"], slot_sum, routed)
     torch.cuda.synchronize()
     assert_within(bf16_host(routed), O.combine(ref["ids"], ref["slot_y"], None), f"TP2 routed part {over}")
+
+
+@pytest.mark.parametrize("over", CASES, ids=IDS)
+def test_four_rank_split_with_zero_padded_shares(over):
+    """A split of I whose shares are multiples of 32 but not of 128 (I = 384 over four ranks: 96 each, as
+    2304 over four gives 576): each rank's share is widened to 128 with zero codes (synth.pad_inter), which
+    the library takes, and the four fp32 partials sum to the layer within the layer tolerance."""
+    over = dict(over, I=384)
+    cfg, inp = inputs(0, **over)
+    d = upload(inp)
+    r = _route(cfg, d)
+    M, k, H, G = cfg.M, cfg.k, cfg.H, 4
+    Ig, Ipad = cfg.I // G, 128
+    rdims = dims_of(synth.get_config(0, **dict(over, I=Ipad)))
+    rws = m().workspace(rdims, M)
+    slot_sum = torch.zeros((M * k, H), dtype=torch.float32, device="cuda")
+    sh_sum = torch.zeros((M, H), dtype=torch.float32, device="cuda")
+    for rank in range(G):
+        dr = upload(synth.pad_inter(_rank_slices(inp, cfg, rank, G), Ig, Ipad))
+        part = torch.empty((M * k, H), dtype=torch.float32, device="cuda")
+        shp = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        m().moe_expert_ffn_f32(rdims, r["xq"], r["xs"], packed_of(dr), None, r["rw"], r["offsets"], r["pairs"],
+                               r["active"], part, rws)
+        m().moe_shared_expert_f32(rdims, r["xq"], r["xs"], shared_of(dr), shp, rws)
+        slot_sum += part
+        sh_sum += shp
+    out = torch.empty((M, H), dtype=torch.int16, device="cuda")
+    m().moe_combine_official_f32(r["dims"], r["ids"], slot_sum, out, shared_f32=sh_sum)
+    routed = torch.empty_like(out)
+    m().moe_combine_official_f32(r["dims"], r["ids"], slot_sum, routed)
+    torch.cuda.synchronize()
+    ids, rw = r["ids"].cpu().numpy(), r["rw"].cpu().numpy()
+    ref = O.moe_forward(inp, cfg)
+    diff = check_routing(ids, rw, ref["route"], cfg)
+    if diff.size:
+        ref = O.moe_forward(inp, cfg, ids=ids, rw=rw)
+    mx, l2 = assert_within(bf16_host(out), ref["out"], f"TP4 padded {over}")
+    assert_within(bf16_host(routed), O.combine(ref["ids"], ref["slot_y"], None), f"TP4 padded routed part {over}")
+    print(f"TP4 (shares of 96 padded to 128) {over}: max-err ratio {mx:.3g}, rel-L2 {l2:.3g}")

@@ -190,3 +190,22 @@ def test_fp8_linear_equals_exact_integer_sums():
         for n in (0, 31, 32, 255):
             row = exact.fp8_row(inp["w"][n], inp["s"][n // 32])
             assert exact.to_bf16(exact.dot_fixed(xdeq, row)) == o["y"][t, n]
+
+
+@pytest.mark.parametrize("I, I_pad", [(96, 128), (160, 256), (64, 128)])
+def test_zero_padding_of_the_intermediate_width_changes_no_output(I, I_pad):
+    """Widening I with zero weight codes leaves every output value unchanged (the library takes I in
+    multiples of 128; an I that is only a multiple of 32, e.g. a quarter of 2304, is padded this way)."""
+    cfg = synth.get_config(0, I=I, shared=True, M=6, seed=11)
+    inp = synth.make_inputs(cfg)
+    pad = synth.pad_inter(inp, I, I_pad)
+    pcfg = synth.get_config(0, I=I_pad, shared=True, M=6, seed=11)
+    a, b = moe.moe_forward(inp, cfg), moe.moe_forward(pad, pcfg)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(b["g"][..., :I], a["g"]) and not np.any(b["g"][..., I:])
+    assert np.array_equal(b["u"][..., :I], a["u"]) and not np.any(b["u"][..., I:])
+    assert np.array_equal(b["h16"][..., :I], a["h16"]) and not np.any(b["h16"][..., I:])
+    # values, not bits: an all-zero sum may come out as -0 on one side and +0 on the other
+    assert np.array_equal(a["slot_y"], b["slot_y"])
+    assert np.array_equal(a["shared_y"], b["shared_y"])
+    assert np.array_equal(a["out"], b["out"])
