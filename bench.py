@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published (E4M3 x E2M1 issues at the FP8 rate)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m8192": 3,
              "prefill_shared_skew_m2048": 4}
@@ -452,6 +453,99 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
     return res
 
 
+def measure_decoded(cid: int, steps: int, warmup: int, packed_ms=None) -> dict:
+    """The decoded-BF16 arm on one workload: the routed experts expanded once to bf16 (moe_expand_mxfp4) and
+    the layer run on them (routed only, no shared expert), K timed steps after W warm-up steps, and GEMM1 /
+    GEMM2 alone through the split entry points with HIP events, against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import mxfp4_routed_expert_moe_amd as moe
+    import synth
+
+    cfg = synth.get_config(cid)
+    inp = synth.make_inputs(cfg)
+    E, H, I, k, M = cfg.E, cfg.H, cfg.I, cfg.k, cfg.M
+
+    def up(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x, gw, gb = up(inp["x"]), up(inp["gate_w"]), up(inp["gate_b"])
+    dims = moe.Dims(E, H, I, k, cfg.route_scale)
+    dec = moe.BF16Experts(*(torch.empty(s, dtype=torch.int16, device="cuda") for s in [(E, I, H), (E, I, H), (E, H, I)]))
+    for n, sn, dst in (("w1", "s1", dec.w1), ("w3", "s3", dec.w3), ("w2", "s2", dec.w2)):
+        w, sc = up(inp[n]), up(inp[sn])
+        moe.moe_expand_mxfp4(w, sc, dst)
+        torch.cuda.synchronize()
+        del w, sc
+    del inp
+    torch.cuda.empty_cache()
+    dev = dict(device="cuda")
+    ws = moe.workspace(dims, M)
+    out = torch.empty((M, H), dtype=torch.int16, **dev)
+    ids = torch.empty((M, k), dtype=torch.int32, **dev)
+    rw = torch.empty((M, k), dtype=torch.float32, **dev)
+    xq = torch.empty((M, H), dtype=torch.uint8, **dev)
+    xs = torch.empty((M, H // 32), dtype=torch.uint8, **dev)
+    counts = torch.empty(E, dtype=torch.int32, **dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, **dev)
+    pairs = torch.empty(M * k, dtype=torch.int32, **dev)
+    active = torch.empty(E, dtype=torch.int32, **dev)
+    hq = torch.empty((M * k, I), dtype=torch.uint8, **dev)
+    hs = torch.empty((M * k, I // 32), dtype=torch.uint8, **dev)
+    slot = torch.empty((M * k, H), dtype=torch.int16, **dev)
+
+    def layer():
+        moe.moe_forward(dims, x, gw, gb, None, dec, None, out, ids, rw, None, ws)
+
+    for _ in range(warmup):
+        layer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    moe.moe_route(dims, x, gw, gb, ids, rw, xq, xs, ws)
+    moe.moe_permute(dims, ids, counts, offsets, pairs, None, active)
+
+    def timed(f, n):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    n = max(3, steps // 2)
+    g1_us = timed(lambda: moe.moe_expert_gemm1(dims, xq, xs, None, dec, rw, offsets, pairs, active, hq, hs, ws), n)
+    g2_us = timed(lambda: moe.moe_expert_gemm2(dims, M, hq, hs, None, dec, offsets, pairs, active, slot, ws), n)
+    f13, f2 = _flops_per_pair(cfg)
+    P = M * k
+    g1_tf = P * f13 / (g1_us * 1e-6) / 1e12
+    res = dict(workload=cfg.name, M=M, arm="decoded-BF16 (expanded weights, bf16 MFMA grouped GEMM)",
+               value=round(M / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+               steps=steps, warmup=warmup, decoded_weight_bytes=3 * E * H * I * 2,
+               kernel_us=dict(gemm1=round(g1_us, 1), gemm2=round(g2_us, 1)),
+               layer_tflops=round(P * (f13 + f2) / (ms * 1e-3) / 1e12, 1),
+               roofline=dict(kernel="expert_gemm_bf16 GEMM1 (w1/w3 + SwiGLU + QDQ)", bound="mfma",
+                             achieved=round(g1_tf, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(g1_tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                             algorithmic_flops=P * f13, avg_us=round(g1_us, 1),
+                             avg_us_timing=f"HIP events around {n} back-to-back launches"),
+               note="routed experts only (the workload has no shared expert); same routing as the packed arm")
+    if packed_ms:
+        res["vs_packed_arm"] = round(packed_ms / ms, 4)
+    del dec, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def leg(r: dict) -> dict:
     """The JSON object of one workload measured by measure() (value = tokens/s of the K-step loop)."""
     return dict(workload=r["workload"], M=r["M"], value=round(r["tokens_per_s"], 1), unit="tokens/s",
@@ -666,6 +760,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FP8 projection family")
     ap.add_argument("--no-widths", action="store_true", help="skip the verifier widths M = 1 .. 32")
     ap.add_argument("--no-peaks", action="store_true", help="skip the HBM-read and MFMA peak microbenchmarks")
+    ap.add_argument("--no-decoded", action="store_true",
+                    help="skip the decoded-BF16 arm at the 8192-token prefill workload")
     ap.add_argument("--stored-layout", action="store_true",
                     help="stream the weight codes (routed experts and the dense FP8 family) from their stored "
                          "row-major layout instead of the fragment-order copy made at load")
@@ -716,6 +812,13 @@ def main():
         others[name] = leg(r)
         print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, samples {r['step_us']}, kernels "
               f"{ {k: round(v, 1) for k, v in r['kernel_us'].items()} }", file=sys.stderr, flush=True)
+    decoded = None
+    if not args.no_decoded and not args.no_prefill:
+        pre = others.get("prefill_m8192")
+        decoded = measure_decoded(WORKLOADS["prefill_m8192"], max(10, args.steps // 10), max(2, args.warmup // 5),
+                                  pre["ms_per_step"] if pre else None)
+        print(f"# decoded-BF16 arm, prefill_m8192: {decoded['ms_per_step']:.3f} ms/step, kernels "
+              f"{decoded['kernel_us']}", file=sys.stderr, flush=True)
     dense = None
     if not args.no_dense:
         dense = measure_dense(tiled=tiled)
@@ -763,6 +866,7 @@ def main():
         "prefill": others.get("prefill_m8192"),
         "batched_decode_m64": others.get("batched_decode_m64"),
         "prefill_shared_skew_m2048": others.get("prefill_shared_skew_m2048"),
+        "decoded_bf16_prefill_m8192": decoded,
         "verifier_widths": r.get("widths"),
         "dense_fp8": dense,
         "peaks": peaks,

@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "expert_wide.hip", "combine.hip",
+SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "expert_mfma.hip", "expert_wide.hip", "expert_bf16.hip",
+           "combine.hip",
            "expand.hip", "dense.hip", "moe_abi.cpp"]
 
 # test-only probes: source under tests/csrc -> tests/lib<name>.so

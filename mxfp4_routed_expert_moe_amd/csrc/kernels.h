@@ -87,6 +87,14 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 void launch_gemm1_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
 void launch_gemm2_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s);
 
+// ---- decoded-BF16 arm at prefill widths (expert_bf16.hip) ---------------------------------------
+// The routed problems of the *_small launchers with W_BF16 weights on the bf16 matrix cores, over the row-tile
+// list of launch_tile_map; activation scales and h_s row-major.
+void launch_gemm1_bf16(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
+                       const int32_t* info, hipStream_t s);
+void launch_gemm2_bf16(const GemmProblem& p, int max_tiles, const int32_t* tile_e, const int32_t* tile_r0,
+                       const int32_t* info, hipStream_t s);
+
 // ---- expert GEMMs on the block-scaled matrix cores (expert_mfma.hip) ---------------------------
 // Upper bound of the row-tile list for P (token, slot) pairs over E experts.
 int mfma_max_tiles(int P, int E);

@@ -136,11 +136,15 @@ moe_status check_shared(const moe_fp8_expert* w) {
 }
 
 // ---- launch sequences (arguments already validated) ------------------------------------------
-// Kernel variant: a pure function of (dims, M). The block-scaled MFMA grouped GEMM once the experts
-// hold 32 rows on average (prefill); the weight-streaming kernel at decode width and for the
-// decoded-BF16 arm.
+// Kernel variant: a pure function of (dims, M) and the arm. Once the experts hold 32 rows on average
+// (prefill widths) the grouped GEMMs over the row-tile list: block-scaled MFMA for the packed experts,
+// bf16 MFMA for the decoded-BF16 arm. Below, the weight-streaming kernels (packed) and the per-expert
+// vector kernel (decoded).
+inline bool routed_tiled(const moe_dims* d, int M) {
+  return (int64_t)M * d->top_k >= 32 * (int64_t)d->num_experts;
+}
 inline bool routed_mfma(const moe_dims* d, int M, const moe_mxfp4_experts* packed) {
-  return packed != nullptr && (int64_t)M * d->top_k >= 32 * (int64_t)d->num_experts;
+  return packed != nullptr && routed_tiled(d, M);
 }
 inline bool shared_mfma(int M) { return M > 64; }
 // The 512 x 128 tile kernels (expert_wide.hip) serve the fragment-order MXFP4 copy at prefill width while every
@@ -237,6 +241,7 @@ void do_gemm1(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* xs, co
     else moe::launch_gemm1_mfma(f, p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   }
   else if (packed) moe::launch_gemm1_stream(f, p, max_active, s);
+  else if (routed_tiled(d, M)) moe::launch_gemm1_bf16(p, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   else moe::launch_gemm1_small(f, p, max_active, s);
 }
 
@@ -267,7 +272,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
   q.act_q = hq; q.act_s = hs; q.act_by_token = 0;
   q.out = slot; q.out_f32 = slot_f32;
   // (out_rows: the decode-width kernels only; the caller passes it only when no prefill-width kernel runs)
-  q.out_rows = routed_mfma(d, M, packed) ? nullptr : out_rows;
+  q.out_rows = routed_tiled(d, M) ? nullptr : out_rows;
   if (routed_mfma(d, M, packed)) {
     if (packed->stage_scales != nullptr) {
       q.sa = packed->stage_scales + stage_scales_off(d, 2);
@@ -289,6 +294,7 @@ void do_gemm2(const moe_dims* d, int M, const uint8_t* hq, const uint8_t* hs, co
     }
   }
   else if (packed) moe::launch_gemm2_stream(f, q, max_active, s);
+  else if (routed_tiled(d, M)) moe::launch_gemm2_bf16(q, tm.max_tiles, tm.tile_e, tm.tile_r0, tm.info, s);
   else moe::launch_gemm2_small(f, q, max_active, s);
 }
 
@@ -300,9 +306,9 @@ void do_expert_ffn(const moe_dims* d, int M, const uint8_t* xq, const uint8_t* x
                    void* ws, hipStream_t s,
                    const int32_t* out_rows = nullptr) {
   TileMap tm;
-  if (routed_mfma(d, M, packed)) {
+  if (routed_tiled(d, M)) {
     tm = make_tile_map(d, M, offsets, ws, s);
-    tm.act_sm = h_internal;
+    tm.act_sm = h_internal && packed != nullptr;   // the bf16 kernels keep h_s row-major
   }
   do_gemm1(d, M, xq, xs, packed, decoded, rw, offsets, pairs, active, hq, hs, tm, s);
   do_gemm2(d, M, hq, hs, packed, decoded, offsets, pairs, active, slot, slot_f32, tm, s, out_rows);
@@ -374,7 +380,7 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   // decode widths on the decode-width kernels: each token's slot rows are written in ascending expert-id order
   // (rows from the selection kernel), so the combine reads no ids
-  const bool ranked = M <= moe::kRouterSmallM && !routed_mfma(dims, M, packed);
+  const bool ranked = M <= moe::kRouterSmallM && !routed_tiled(dims, M);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
                 at<uint8_t>(ws, L.h_s), true, ws, s, ranked ? at<int32_t>(ws, L.out_rows) : nullptr);
   uint16_t* sh_out = nullptr;
@@ -500,7 +506,7 @@ moe_status moe_expert_gemm1(const moe_dims* dims, int32_t M, const uint8_t* x_q,
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   TileMap tm;
-  if (routed_mfma(dims, M, packed)) tm = make_tile_map(dims, M, offsets, ws, s);
+  if (routed_tiled(dims, M)) tm = make_tile_map(dims, M, offsets, ws, s);
   do_gemm1(dims, M, x_q, x_s, packed, decoded, rw, offsets, pairs, active, h_q, h_s, tm, s);
   return launched();
 }
@@ -518,7 +524,7 @@ moe_status moe_expert_gemm2(const moe_dims* dims, int32_t M, const uint8_t* h_q,
   MOE_TRY(check_ws(dims, M, ws, ws_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   TileMap tm;
-  if (routed_mfma(dims, M, packed)) tm = make_tile_map(dims, M, offsets, ws, s);
+  if (routed_tiled(dims, M)) tm = make_tile_map(dims, M, offsets, ws, s);
   do_gemm2(dims, M, h_q, h_s, packed, decoded, offsets, pairs, active, slot_out, nullptr, tm, s);
   return launched();
 }
