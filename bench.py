@@ -42,8 +42,8 @@ WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m81
 # were measured on (sha256 prefix); after any change to it the traffic is reported as null until re-measured.
 FETCH_SCALE, WRITE_SCALE = 1048576 / 524300.9, 1.0
 MEASURED_TRAFFIC = {
-    "decode_m8": dict(src="expert_gemm.hip", sha="129a4bb763d14ee8", fetch_kib=228000.9, write_kib=135.2),
-    "prefill_m8192": dict(src="expert_mfma.hip", sha="2adfd3c215134d8e", fetch_kib=1784893.9, write_kib=166161.4),
+    "decode_m8": dict(src="expert_gemm.hip", sha="6172cafb71718d05", fetch_kib=227858.4, write_kib=135.1),
+    "prefill_m8192": dict(src="expert_wide.hip", sha="0068fe82265a2b5c", fetch_kib=1498531.8, write_kib=114387.0),
 }
 
 
@@ -267,12 +267,15 @@ class Telemetry:
         def num(k):
             v = m.get(k)
             return v if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF) else None
-        gfx = num("current_gfxclk")
-        if gfx is None and isinstance(m.get("current_gfxclks"), list):
+        gfx = None
+        if isinstance(m.get("current_gfxclks"), list):   # one clock per XCD: their mean
             vals = [v for v in m["current_gfxclks"] if isinstance(v, int) and 0 < v < 0xFFFF]
             gfx = sum(vals) / len(vals) if vals else None
-        return dict(gfx_mhz=gfx, mem_mhz=num("current_uclk"), power_w=num("current_socket_power") or
-                    num("average_socket_power"), hotspot_c=num("temperature_hotspot"))
+        if gfx is None:
+            gfx = num("current_gfxclk")
+        return dict(gfx_mhz=gfx, avg_gfx_mhz=num("average_gfxclk_frequency"), gfx_activity_pct=num("average_gfx_activity"),
+                    mem_mhz=num("current_uclk"), power_w=num("current_socket_power") or num("average_socket_power"),
+                    hotspot_c=num("temperature_hotspot"))
 
     def _run(self):
         while not self._stop.is_set():
@@ -298,7 +301,7 @@ class Telemetry:
         if not self.samples:
             return None
         out = dict(samples=len(self.samples), period_ms=self.period * 1e3, source="amdsmi gpu metrics")
-        for k in ("gfx_mhz", "mem_mhz", "power_w", "hotspot_c"):
+        for k in ("gfx_mhz", "avg_gfx_mhz", "gfx_activity_pct", "mem_mhz", "power_w", "hotspot_c"):
             v = sorted(x[k] for x in self.samples if x.get(k) is not None)
             out[k] = None if not v else dict(min=v[0], median=v[len(v) // 2], max=v[-1])
         return out
@@ -558,15 +561,16 @@ def leg(r: dict) -> dict:
 
 
 def measure_peaks() -> dict:
-    """This GPU's achievable peaks for the two rooflines (libpeaks.so, built with the library): a read of
-    2 GiB with 16-byte non-temporal loads, and dependency-free streams of the scaled 16x16x128 MFMA for the
-    three operand-format pairs, on every SIMD (512 blocks of 4 waves)."""
+    """This GPU's achievable peaks for the two rooflines (libpeaks.so, built with the library): the best read of
+    2 GiB over a sweep of block counts, loads in flight and the non-temporal hint, and dependency-free streams
+    of the scaled 16x16x128 MFMA for the three operand-format pairs, on every SIMD (512 blocks of 4 waves)."""
     import ctypes
 
     import torch
 
     lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "libpeaks.so"))
-    lib.moe_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_void_p]
     st = torch.cuda.current_stream().cuda_stream
@@ -586,10 +590,19 @@ def measure_peaks() -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e-3 / reps
 
-    t = timed(lambda: lib.moe_peak_stream_read(buf.data_ptr(), n, sink.data_ptr(), st), 10)
-    out = dict(stream_read=dict(bytes=n, gbs=round(n / t / 1e9, 1), frac_of_8tbs=round(n / t / 8e12, 4),
+    sweep = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        for unroll in (8, 16):
+            for nt in (0, 1):
+                t = timed(lambda: lib.moe_peak_stream_read(buf.data_ptr(), n, blocks, unroll, nt, sink.data_ptr(),
+                                                           st), 10)
+                sweep[f"b{blocks}_u{unroll}_{'nt' if nt else 'plain'}"] = round(n / t / 1e9, 1)
+    best = max(sweep, key=sweep.get)
+    out = dict(stream_read=dict(bytes=n, gbs=sweep[best], frac_of_8tbs=round(sweep[best] / 8000, 4), best=best,
+                                sweep_gbs=sweep,
                                 method="2 GiB read once per call, each wave a contiguous run of 1 KB loads "
-                                       "(16-byte non-temporal loads per lane), 10 calls"))
+                                       "(16-byte loads per lane); blocks x loads in flight x hint swept, "
+                                       "the best kept; 10 calls each"))
     del buf
     blocks, iters = 512, 4096
     fsink = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")

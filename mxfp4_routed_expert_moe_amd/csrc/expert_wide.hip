@@ -20,7 +20,7 @@
 // Data flow. Each weight row is used by one wave only, so the weights go straight from the fragment-order
 // copy into registers (one 1 KB contiguous load per 16-row fragment and step), two steps ahead of their use
 // in three rotating register sets. The activation rows (shared by the four waves) and the E8M0 bytes of both
-// operands go into a six-slot LDS ring by direct global-to-LDS copies, three steps ahead. The activation
+// operands go into a three-slot LDS ring by direct global-to-LDS copies, two steps ahead. The activation
 // copies place each 16-row fragment in the order its MFMA lanes read it, so every fragment read is one
 // conflict-free 16-byte read per lane and half. Every wave issues the same five copies and eight loads per
 // step, always (steps past the last re-read the last one), so one exact wait count covers the ring: at the

@@ -1,7 +1,8 @@
 // Peak-rate microbenchmarks of the two rooflines the layer is measured against, on this GPU (a bench-only
 // library, libpeaks.so; not part of libmoe.so):
-//   moe_peak_stream_read - every byte of a device buffer read once with 16-byte non-temporal loads per lane,
-//                          the access the decode-width GEMMs make of the packed weights;
+//   moe_peak_stream_read - every byte of a device buffer read once with 16-byte loads per lane (optionally
+//                          non-temporal), the access the decode-width GEMMs make of the packed weights; the
+//                          caller sweeps the block count and loads in flight and keeps the best;
 //   moe_peak_mfma        - a dependency-free stream of v_mfma_scale_f32_16x16x128_f8f6f4 on every SIMD, for a
 //                          pair of operand formats (E2M1 x E4M3 is the pair of the routed experts).
 // Both write one value per wave or block so that no load or MFMA is removed.
@@ -14,28 +15,33 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kReadBlocks = 4096;
-constexpr int kReadUnroll = 8;
+constexpr int kMaxReadBlocks = 8192;
 
-// Each wave reads a contiguous run of the buffer, 1 KB per load instruction (16 bytes per lane), kReadUnroll
-// loads in flight, as a decode GEMM wave streams its weight fragments; XOR-folded into one dword per block.
+// Each wave reads a contiguous run of the buffer, 1 KB per load instruction (16 bytes per lane), UNROLL loads
+// in flight, as a decode GEMM wave streams its weight fragments (NT: with the non-temporal hint);
+// XOR-folded into one dword per block.
+template <int UNROLL, bool NT>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
                                                           unsigned* __restrict__ sink) {
   const size_t waves = (size_t)gridDim.x * 4;
   const size_t wave = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const size_t per = (n16 / 64 + waves - 1) / waves;   // 1 KB pieces per wave
-  const size_t p0 = wave * per, p1 = min(p0 + per, n16 / 64);
+  const size_t p0 = min(wave * per, n16 / 64), p1 = min(p0 + per, n16 / 64);
+  auto ld = [&](size_t i) {
+    if constexpr (NT) return __builtin_nontemporal_load(buf + i);
+    else return buf[i];
+  };
   unsigned x = 0;
   size_t q = p0;
-  for (; q + kReadUnroll <= p1; q += kReadUnroll) {
-    u32x4 v[kReadUnroll];
+  for (; q + UNROLL <= p1; q += UNROLL) {
+    u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + (q + u) * 64 + lane);
+    for (int u = 0; u < UNROLL; ++u) v[u] = ld((q + u) * 64 + lane);
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < UNROLL; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; q < p1; ++q) {
-    const u32x4 v = __builtin_nontemporal_load(buf + q * 64 + lane);
+    const u32x4 v = ld(q * 64 + lane);
     x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   __shared__ unsigned red[256];
@@ -75,15 +81,23 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* __rest
 
 extern "C" {
 
-// Number of dwords the sink of moe_peak_stream_read must hold.
-int moe_peak_stream_blocks(void) { return kReadBlocks; }
+// Number of dwords the sink of moe_peak_stream_read must hold (the largest block count it takes).
+int moe_peak_stream_blocks(void) { return kMaxReadBlocks; }
 
-// Reads `bytes` (a multiple of 1024) of the device buffer `buf` once; sink: device, moe_peak_stream_blocks()
-// dwords. Returns 0, -1 for a bad argument, -4 if the launch failed.
-int moe_peak_stream_read(const void* buf, size_t bytes, unsigned* sink, void* stream) {
-  if (!buf || !sink || bytes % 1024 != 0) return -1;
-  stream_read_kernel<<<dim3(kReadBlocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const u32x4*>(buf), bytes / 16, sink);
+// Reads `bytes` (a multiple of 1024) of the device buffer `buf` once with `blocks` blocks of 4 waves (1 ..
+// moe_peak_stream_blocks()), `unroll` loads in flight per wave (8 or 16), with the non-temporal hint if nt;
+// sink: device, moe_peak_stream_blocks() dwords. Returns 0, -1 for a bad argument, -4 if the launch failed.
+int moe_peak_stream_read(const void* buf, size_t bytes, int blocks, int unroll, int nt, unsigned* sink, void* stream) {
+  if (!buf || !sink || bytes % 1024 != 0 || blocks < 1 || blocks > kMaxReadBlocks) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* b = static_cast<const u32x4*>(buf);
+  const size_t n16 = bytes / 16;
+  const dim3 g(blocks), t(256);
+  if (unroll == 8 && nt) stream_read_kernel<8, true><<<g, t, 0, s>>>(b, n16, sink);
+  else if (unroll == 8) stream_read_kernel<8, false><<<g, t, 0, s>>>(b, n16, sink);
+  else if (unroll == 16 && nt) stream_read_kernel<16, true><<<g, t, 0, s>>>(b, n16, sink);
+  else if (unroll == 16) stream_read_kernel<16, false><<<g, t, 0, s>>>(b, n16, sink);
+  else return -1;
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
