@@ -598,11 +598,22 @@ def measure_peaks() -> dict:
                                                            st), 10)
                 sweep[f"b{blocks}_u{unroll}_{'nt' if nt else 'plain'}"] = round(n / t / 1e9, 1)
     best = max(sweep, key=sweep.get)
+    lib.moe_peak_l2_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    l2 = {}
+    for windows in (16, 32):   # 1 MB and 2 MB of windows: resident in each XCD's 4 MB L2
+        for blocks in (1024, 2048):
+            reps = 64
+            t = timed(lambda: lib.moe_peak_l2_read(buf.data_ptr(), windows, blocks, reps, sink.data_ptr(), st), 5)
+            l2[f"w{windows}_b{blocks}"] = round(blocks * 4 * reps * 65536 / t / 1e9, 1)
     out = dict(stream_read=dict(bytes=n, gbs=sweep[best], frac_of_8tbs=round(sweep[best] / 8000, 4), best=best,
                                 sweep_gbs=sweep,
                                 method="2 GiB read once per call, each wave a contiguous run of 1 KB loads "
                                        "(16-byte loads per lane); blocks x loads in flight x hint swept, "
-                                       "the best kept; 10 calls each"))
+                                       "the best kept; 10 calls each"),
+               l2_read=dict(gbs=max(l2.values()), sweep_gbs=l2,
+                            method="each wave re-reads a 64 KB window of a 1 or 2 MB buffer 64 times (L2-resident), "
+                                   "1 KB per load instruction, 16 loads in flight"))
     del buf
     blocks, iters = 512, 4096
     fsink = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")

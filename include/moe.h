@@ -47,6 +47,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Kernel family of the routed GEMMs, a function of (dims, M) only: while M * top_k is below
+ * MOE_TILED_ROWS_PER_EXPERT * num_experts (fewer than that many rows per expert on average) the weights
+ * stream through the decode-width kernels (each expert's rows in passes of up to 8); from there on the
+ * GEMMs run over a row-tile list of 128 rows per expert tile. Outputs stay within the stated tolerance
+ * on either side; their bits can change where M crosses the boundary (the fp32 summation order differs). */
+#define MOE_TILED_ROWS_PER_EXPERT 6
+
 #ifdef __cplusplus
 extern "C" {
 #endif

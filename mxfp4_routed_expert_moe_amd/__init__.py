@@ -22,7 +22,7 @@ __all__ = [
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
     "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
     "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights", "moe_fp8_tiled_weights_bytes",
-    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "TILED_ROWS_PER_EXPERT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -341,6 +341,9 @@ def moe_forward(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, deco
 
 # size of the library-owned workspace of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES in moe.h)
 NOALLOC_SCRATCH_BYTES = 16 << 20
+# the routed GEMMs run over the row-tile list once M * top_k >= TILED_ROWS_PER_EXPERT * num_experts
+# (MOE_TILED_ROWS_PER_EXPERT in moe.h)
+TILED_ROWS_PER_EXPERT = 6
 
 
 def moe_forward_noalloc(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, decoded: BF16Experts | None,

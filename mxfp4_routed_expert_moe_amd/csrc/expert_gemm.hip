@@ -227,7 +227,7 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 // a contiguous run of bytes), prefetching kStreamU steps ahead, so the only vector-memory traffic in
 // the loop is the wave's own weight rows. The E8M0 scales of the 64 rows and up to 4 activation rows
 // of the expert (E4M3 codes and scales) are staged in LDS at the start; experts with more rows are
-// processed 4 rows at a time. GEMM1's w1 and w3 fragments meet in LDS for the SwiGLU/QDQ epilogue, which
+// processed kRows (4 or 8) rows at a time. GEMM1's w1 and w3 fragments meet in LDS for the SwiGLU/QDQ epilogue, which
 // two waves share; GEMM2's waves store their own rows.
 //
 // Operand layout (measured on gfx950): lane l = (row l % 16, group g = l / 16); an E2M1 operand
@@ -237,7 +237,11 @@ void launch_gemm2_small(WeightFormat f, const GemmProblem& p, int max_active, hi
 // =================================================================================================
 namespace {
 
-constexpr int kStreamRows = 4;   // activation rows staged in LDS per pass
+// activation rows staged in LDS per pass (the MFMA's 16 columns hold up to 16): 4 while the experts average
+// fewer than three rows, which keeps the staging small enough for four blocks per CU; 8 above, so that experts
+// with 5 .. 8 rows stream their weights once instead of twice (full-size layer, 8 against 4 rows: M = 64 494 ->
+// 452 us, M = 128 720 -> 569 us, M = 256 1234 -> 881 us; M = 48 401 -> 404 us, hence the threshold)
+constexpr int kStreamRowsFew = 4, kStreamRowsMany = 8;
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for
 // vmcnt(0) lgkmcnt(0), expcnt left at its maximum (not waited for)
 constexpr int kWaitVmLgkm0 = 0x7 << 4;
@@ -294,12 +298,12 @@ struct StreamA<W_FP8_BLOCK32> {
 
 }  // namespace
 
-// Dynamic LDS: scales [64][K/32], activation codes [4][K], activation scales [4][K/32], then the
+// Dynamic LDS: scales [64][K/32], activation codes [kRows][K], activation scales [kRows][K/32], then the
 // [4 waves][64 lanes] fp32x4 exchange of the fragments and the [2][16] amax halves (GEMM1).
 // kStreamU: K steps per weight register set (two sets alternate). 4 by default; 3 where the step count is a
 // multiple of 6 and not of 8 (w2 at I = 2304: 18 steps), so that no batch of loads re-reads past the last step
 // (decode layer: GEMM2 40.8 -> 39.4 us, interleaved A/B on one box).
-template <int WF, bool GEMM1, bool TILED, int kStreamU = 4>
+template <int WF, bool GEMM1, bool TILED, int kStreamU = 4, int kRows = kStreamRowsFew>
 __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   static_assert(!TILED || WF == W_MXFP4, "the fragment-order copy holds MXFP4 codes");
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -317,9 +321,9 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   }
   const int K = p.K, nk = K / 128, KB = K / 32;
   uint8_t* sc = dyn;                                   // [64][KB]
-  uint8_t* xb = sc + 64 * KB;                          // [4][K]
-  uint8_t* xsb = xb + kStreamRows * K;                 // [4][KB]
-  f32x4* xch = reinterpret_cast<f32x4*>(dyn + ((64 * KB + kStreamRows * (K + KB) + 15) & ~15));   // [4][64]
+  uint8_t* xb = sc + 64 * KB;                          // [kRows][K]
+  uint8_t* xsb = xb + kRows * K;                       // [kRows][KB]
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn + ((64 * KB + kRows * (K + KB) + 15) & ~15));   // [4][64]
   float* amx = reinterpret_cast<float*>(xch + 4 * 64);                                            // [2][16]
   // block rows: GEMM1 output columns c0 .. c0 + 31 (LDS rows 0..31 = w1, 32..63 = w3); GEMM2 rows c0 .. c0 + 63
   const int c0 = GEMM1 ? blockIdx.x * 32 : blockIdx.x * 64;
@@ -333,8 +337,8 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   const uint8_t* wsrc = TILED ? wmat + ((size_t)(grow_of(lrow) >> 4) * nk) * 1024 + 16 * lane
                               : wmat + (size_t)grow_of(lrow) * wrow_bytes + 16 * g;
 
-  for (int tg = 0; tg < nrows; tg += kStreamRows) {
-    const int n = min(kStreamRows, nrows - tg);
+  for (int tg = 0; tg < nrows; tg += kRows) {
+    const int n = min(kRows, nrows - tg);
     // staging: runs of contiguous bytes copied straight into LDS, one run per wave in turn, all in
     // flight together. Run 0/1: the weight scales (MXFP4: the 64 rows' E8M0 bytes, two K-byte runs for
     // GEMM1 (w1, w3 rows) or one 2K-byte run for GEMM2; FP8: the two 32-row blocks' scale rows). Then
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
     // before every use of a weight register, leaving only one batch of steps in flight.
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
     __builtin_amdgcn_s_barrier();
-    const int bt = r16 & (kStreamRows - 1);   // lanes past the staged rows compute a staged row (discarded)
+    const int bt = r16 & (kRows - 1);   // lanes past the staged rows compute a staged row (discarded)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     auto run = [&](const StreamA<WF> (&R)[kStreamU], int ks0) {
 #pragma unroll
@@ -469,23 +473,39 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
   }
 }
 
-size_t stream_lds_bytes(int K) {
+size_t stream_lds_bytes(int K, int rows) {
   const int KB = K / 32;
-  return (size_t)((64 * KB + kStreamRows * (K + KB) + 15) & ~15) + 4 * 64 * sizeof(f32x4) + 32 * sizeof(float);
+  return (size_t)((64 * KB + rows * (K + KB) + 15) & ~15) + 4 * 64 * sizeof(f32x4) + 32 * sizeof(float);
+}
+
+// Rows per pass: a function of (M, k, E) only, so launch geometry never depends on routed data. The per-row
+// arithmetic (the same MFMAs over the same K steps) does not depend on it, so outputs are identical either way.
+static int stream_rows(const GemmProblem& p) {
+  if (p.dense) return p.M > kStreamRowsFew ? kStreamRowsMany : kStreamRowsFew;
+  return (long long)p.M * p.k >= 3LL * p.num_experts ? kStreamRowsMany : kStreamRowsFew;
+}
+
+template <int WF, bool GEMM1, bool TILED, int U>
+static void launch_stream_rows(const GemmProblem& p, dim3 grid, hipStream_t s) {
+  const int rows = stream_rows(p);
+  const size_t lds = stream_lds_bytes(p.K, rows);
+  if (rows == kStreamRowsMany)
+    expert_gemm_stream<WF, GEMM1, TILED, U, kStreamRowsMany><<<grid, dim3(256), lds, s>>>(p);
+  else
+    expert_gemm_stream<WF, GEMM1, TILED, U, kStreamRowsFew><<<grid, dim3(256), lds, s>>>(p);
 }
 
 template <bool GEMM1>
 static void launch_stream(WeightFormat f, const GemmProblem& p, int max_active, hipStream_t s) {
   dim3 grid(GEMM1 ? p.N / 32 : p.N / 64, p.dense ? 1 : max_active);
-  const size_t lds = stream_lds_bytes(p.K);
   switch (f) {
     case W_MXFP4:
       if (p.w_tiled && (p.K / 128) % 6 == 0 && (p.K / 128) % 8 != 0)
-        expert_gemm_stream<W_MXFP4, GEMM1, true, 3><<<grid, dim3(256), lds, s>>>(p);
-      else if (p.w_tiled) expert_gemm_stream<W_MXFP4, GEMM1, true><<<grid, dim3(256), lds, s>>>(p);
-      else expert_gemm_stream<W_MXFP4, GEMM1, false><<<grid, dim3(256), lds, s>>>(p);
+        launch_stream_rows<W_MXFP4, GEMM1, true, 3>(p, grid, s);
+      else if (p.w_tiled) launch_stream_rows<W_MXFP4, GEMM1, true, 4>(p, grid, s);
+      else launch_stream_rows<W_MXFP4, GEMM1, false, 4>(p, grid, s);
       break;
-    case W_FP8_BLOCK32: expert_gemm_stream<W_FP8_BLOCK32, GEMM1, false><<<grid, dim3(256), lds, s>>>(p); break;
+    case W_FP8_BLOCK32: launch_stream_rows<W_FP8_BLOCK32, GEMM1, false, 4>(p, grid, s); break;
     default: break;   // the bf16 arm uses launch_small
   }
 }

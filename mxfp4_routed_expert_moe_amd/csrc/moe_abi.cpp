@@ -15,6 +15,12 @@ namespace {
 
 using moe::GemmProblem;
 
+// Average rows per expert (M * k / E) from which the routed GEMMs run over the row-tile list. Swept on the
+// full-size layer (E 128, k 6) with the 8-row decode passes: M = 128 561 us streamed against 563-565 us tiled,
+// M = 192 720 against 567, M = 256 888 against 563-575, M = 384 1220 against 573-585, M = 512 1530 against
+// 587-598 us; at M = 64 both 450 us.
+constexpr int kTiledRowsPerExpert = MOE_TILED_ROWS_PER_EXPERT;
+
 // Size of the library-owned workspace of moe_forward_noalloc (per GPU).
 constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
 
@@ -59,10 +65,10 @@ WsLayout ws_layout(const moe_dims* d, int64_t M) {
   L.sh_s = take(m * I / 32);
   L.sh_out = take(m * H * 2);
   // stage-major copies of the routed w1, w3 and w2 scales for the prefill-width GEMMs
-  L.scales = take(m * k >= 32 * E ? 3 * E * I * H / 32 : 0);
+  L.scales = take(m * k >= (size_t)kTiledRowsPerExpert * E ? 3 * E * I * H / 32 : 0);
   // the activation scales of the sorted pairs, stage-major (prefill width: x_s gathered for GEMM1, or a
   // caller's row-major h_s for GEMM2)
-  L.xs_sm = take(m * k >= 32 * E ? m * k * std::max(H, I) / 32 : 0);
+  L.xs_sm = take(m * k >= (size_t)kTiledRowsPerExpert * E ? m * k * std::max(H, I) / 32 : 0);
   L.total = off;
   return L;
 }
@@ -136,12 +142,12 @@ moe_status check_shared(const moe_fp8_expert* w) {
 }
 
 // ---- launch sequences (arguments already validated) ------------------------------------------
-// Kernel variant: a pure function of (dims, M) and the arm. Once the experts hold 32 rows on average
+// Kernel variant: a pure function of (dims, M) and the arm. Once the experts hold kTiledRowsPerExpert rows on average
 // (prefill widths) the grouped GEMMs over the row-tile list: block-scaled MFMA for the packed experts,
 // bf16 MFMA for the decoded-BF16 arm. Below, the weight-streaming kernels (packed) and the per-expert
 // vector kernel (decoded).
 inline bool routed_tiled(const moe_dims* d, int M) {
-  return (int64_t)M * d->top_k >= 32 * (int64_t)d->num_experts;
+  return (int64_t)M * d->top_k >= kTiledRowsPerExpert * (int64_t)d->num_experts;
 }
 inline bool routed_mfma(const moe_dims* d, int M, const moe_mxfp4_experts* packed) {
   return packed != nullptr && routed_tiled(d, M);

@@ -3,6 +3,8 @@
 //   moe_peak_stream_read - every byte of a device buffer read once with 16-byte loads per lane (optionally
 //                          non-temporal), the access the decode-width GEMMs make of the packed weights; the
 //                          caller sweeps the block count and loads in flight and keeps the best;
+//   moe_peak_l2_read     - the same loads from a buffer small enough to stay in every XCD's L2 (the rate at
+//                          which the L2s feed the CUs when they hit);
 //   moe_peak_mfma        - a dependency-free stream of v_mfma_scale_f32_16x16x128_f8f6f4 on every SIMD, for a
 //                          pair of operand formats (E2M1 x E4M3 is the pair of the routed experts).
 // Both write one value per wave or block so that no load or MFMA is removed.
@@ -54,6 +56,34 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   }
 }
 
+// L2-resident reads: wave w reads the 64 KB window (w mod windows) of a small buffer (all windows fit every XCD's
+// L2 after the first pass) reps times, 1 KB per load instruction (16 bytes per lane), 16 loads in flight.
+__global__ __launch_bounds__(256) void l2_read_kernel(const u32x4* __restrict__ buf, int windows, int reps,
+                                                      unsigned* __restrict__ sink) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const u32x4* base = buf + (size_t)(wave % windows) * 4096;   // 64 KB = 4096 x 16 B
+  unsigned x = 0;
+  for (int r = 0; r < reps; ++r) {
+#pragma unroll 1
+    for (int q = 0; q < 64; q += 16) {
+      u32x4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = base[(size_t)(q + u) * 64 + lane];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    x = (x << 1) | (x >> 31);
+  }
+  __shared__ unsigned red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned t = 0;
+    for (int i = 0; i < 256; ++i) t ^= red[i];
+    sink[blockIdx.x] = t;
+  }
+}
+
 // iters x 8 MFMAs per wave on 8 independent accumulators. Operands are finite codes of each format (E4M3 and
 // E2M1 bytes 0x38 / 0x22 with small lane-dependent variation), scales 127 (1.0).
 template <int FA, int FB>
@@ -98,6 +128,16 @@ int moe_peak_stream_read(const void* buf, size_t bytes, int blocks, int unroll, 
   else if (unroll == 16 && nt) stream_read_kernel<16, true><<<g, t, 0, s>>>(b, n16, sink);
   else if (unroll == 16) stream_read_kernel<16, false><<<g, t, 0, s>>>(b, n16, sink);
   else return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// L2-resident read rate: `blocks` blocks (1 .. moe_peak_stream_blocks()) of 4 waves, each wave reading one of
+// `windows` 64 KB windows of `buf` (windows * 64 KB bytes, device) reps times. Bytes read = blocks * 4 * reps *
+// 65536. sink: device, moe_peak_stream_blocks() dwords. Returns 0, -1 for a bad argument, -4 if the launch failed.
+int moe_peak_l2_read(const void* buf, int windows, int blocks, int reps, unsigned* sink, void* stream) {
+  if (!buf || !sink || windows < 1 || blocks < 1 || blocks > kMaxReadBlocks || reps < 1) return -1;
+  l2_read_kernel<<<dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(buf),
+                                                                                   windows, reps, sink);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -281,3 +281,14 @@ def test_dense_workspace_holds_partials_of_split_plans(lib):
     ws = lib.moe_fp8_linear_workspace_bytes(M, N, K)
     # 48 KB / (64 * 132 + 8) = 5 steps per run -> 8 runs of the 40 steps
     assert ws >= 8 * M * N * 4 + M * K + M * K // 32
+
+
+def test_binding_constants_match_the_header():
+    """The Python binding's copies of the header's constants."""
+    import mxfp4_routed_expert_moe_amd as m
+    text = open(HEADER).read()
+    scratch = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    tiled = re.search(r"#define MOE_TILED_ROWS_PER_EXPERT (\d+)", text)
+    assert scratch and tiled
+    assert m.NOALLOC_SCRATCH_BYTES == int(scratch.group(1)) << int(scratch.group(2))
+    assert m.TILED_ROWS_PER_EXPERT == int(tiled.group(1))

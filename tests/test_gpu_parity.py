@@ -362,7 +362,7 @@ def test_all_tokens_on_the_same_experts():
 
 
 # ---------------------------------------------------------------------------------------------
-# the prefill-width path (block-scaled MFMA grouped GEMM): taken when M * k >= 32 * E. Layer sizes
+# the prefill-width path (block-scaled MFMA grouped GEMM): taken when M * k >= TILED_ROWS_PER_EXPERT * E. Layer sizes
 # the oracle computes in full, spanning several row tiles (128) per expert with ragged tails,
 # several column tiles and several K steps (128).
 MFMA_CASES = [
@@ -376,7 +376,7 @@ MFMA_CASES = [
 @pytest.mark.parametrize("over", MFMA_CASES, ids=lambda o: "M{M}_H{H}_I{I}_E{E}_k{k}".format(**o))
 def test_prefill_path_matches_oracle_on_every_token(over, tiled):
     cfg, inp, d = cfg_inputs(0, **over)
-    assert cfg.M * cfg.k >= 32 * cfg.E
+    assert cfg.M * cfg.k >= m().TILED_ROWS_PER_EXPERT * cfg.E
     res = forward(cfg, d, packed=tiled_of(cfg, d) if tiled else None)
     ref = O.moe_forward(inp, cfg)
     diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
@@ -493,12 +493,14 @@ def test_prefill_path_runs_are_bit_identical():
         assert np.array_equal(forward(cfg, d)["out_bits"], a)
 
 
-@pytest.mark.parametrize("M", [1, 5, 37, 64])
+@pytest.mark.parametrize("M", [1, 5, 23, 37, 64])
 def test_decode_width_with_fp8_shared_expert(M):
-    """Decode-width routed experts plus the FP8 shared expert (both through the weight-streaming kernel),
-    every token against the oracle; the routed-only and shared-only parts checked on their own too."""
+    """Decode-width batches with the FP8 shared expert (streamed at every M <= 64), every token against the
+    oracle; the routed-only and shared-only parts checked on their own too. With 8 experts and top-2 the routed
+    part streams up to M = 23 and runs over the row-tile list from M = 24 (6 rows per expert on average)."""
     cfg, inp, d = cfg_inputs(0, M=M, H=512, I=256, E=8, k=2, shared=True)
-    assert cfg.M * cfg.k < 32 * cfg.E
+    tiled = cfg.M * cfg.k >= m().TILED_ROWS_PER_EXPERT * cfg.E
+    assert tiled == (M >= 24)
     res = forward(cfg, d)
     ref = O.moe_forward(inp, cfg)
     diff = check_routing(res["ids"], res["rw"], ref["route"], cfg)
@@ -587,7 +589,7 @@ def test_prepare_mxfp4_scales_layout():
     assert np.array_equal(got, np.concatenate(parts))
 
 
-@pytest.mark.parametrize("over", [dict(M=1000, H=512, I=256, E=8, k=2), dict(M=37, H=512, I=256, E=8, k=2)],
+@pytest.mark.parametrize("over", [dict(M=1000, H=512, I=256, E=8, k=2), dict(M=23, H=512, I=256, E=8, k=2)],
                          ids=["prefill_width", "decode_width"])
 def test_forward_with_prepared_scales_is_identical(over):
     """Passing the prepared stage-major scales changes where the prefill kernels read them, not the
@@ -621,10 +623,11 @@ def test_prepare_mxfp4_weights_layout():
 
 
 TILED_CASES = [dict(M=1000, H=512, I=256, E=8, k=2), dict(M=1000, H=512, I=384, E=8, k=2),
-               dict(M=37, H=512, I=256, E=8, k=2)]
+               dict(M=23, H=512, I=256, E=8, k=2), dict(M=37, H=512, I=256, E=8, k=2)]
 
 
-@pytest.mark.parametrize("over", TILED_CASES, ids=["prefill_width", "prefill_width_I384", "decode_width"])
+@pytest.mark.parametrize("over", TILED_CASES, ids=["prefill_width", "prefill_width_I384", "decode_width",
+                                                  "tiled_at_few_rows"])
 def test_forward_with_tiled_weights_is_identical(over):
     """With the fragment-order copy of the weights (and no row-major weight pointers at all) every GEMM
     reads the same codes from other addresses: outputs equal the call on the stored layout bit for bit,
