@@ -451,6 +451,7 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
                                avg_us=round(gemm1_us, 2), **timing)
     if widths:
         res["widths"] = measure_widths(L, widths, steps, warmup)
+        res["batch_invariant"] = measure_flagged(L, steps, warmup)
     del L
     torch.cuda.empty_cache()
     return res
@@ -547,6 +548,33 @@ def measure_decoded(cid: int, steps: int, warmup: int, packed_ms=None) -> dict:
     del dec, ws
     torch.cuda.empty_cache()
     return res
+
+
+def measure_flagged(L: Layer, steps: int, warmup: int) -> dict:
+    """The same layer with MOE_FLAG_BATCH_INVARIANT (one router summation order at every M): eager loop over the
+    weight replicas, against the default's loop timed the same way right before it."""
+    import dataclasses
+
+    import torch
+
+    flagged = dataclasses.replace(L.dims, flags=L.moe.FLAG_BATCH_INVARIANT)
+
+    def loop(dims):
+        for i in range(warmup):
+            L.moe.moe_forward(dims, L.x, L.gate_w, L.gate_b, L.experts[i % len(L.experts)], None, L.shared, L.out,
+                              L.ids, L.rw, None, L.ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            L.moe.moe_forward(dims, L.x, L.gate_w, L.gate_b, L.experts[i % len(L.experts)], None, L.shared, L.out,
+                              L.ids, L.rw, None, L.ws)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+    default_us = loop(L.dims)
+    flagged_us = loop(flagged)
+    return dict(us=round(flagged_us, 2), default_us=round(default_us, 2),
+                note="router on the matrix-core kernel at every M, selection and permutation as separate kernels")
 
 
 def leg(r: dict) -> dict:
@@ -892,6 +920,7 @@ def main():
         "prefill_shared_skew_m2048": others.get("prefill_shared_skew_m2048"),
         "decoded_bf16_prefill_m8192": decoded,
         "verifier_widths": r.get("widths"),
+        "decode_m8_batch_invariant": r.get("batch_invariant"),
         "dense_fp8": dense,
         "peaks": peaks,
         "cpu_baseline": cpu,

@@ -72,7 +72,18 @@ typedef struct {
   int32_t inter;       /* I: expert intermediate width              */
   int32_t top_k;       /* k: experts per token                      */
   float route_scale;   /* multiplies the normalised route weights   */
+  uint32_t flags;      /* MOE_FLAG_* bits; 0 = default              */
 } moe_dims;
+
+/* Batch invariance. Every stage after the router computes each token's rows with the same arithmetic in the
+ * same order whatever the batch (the streamed and row-tiled GEMMs give the same bits per row), but the router
+ * sums its fp32 logits in one order up to M = 64 tokens (512-wide chunks, 64 lanes' 8-term FMA chains) and in
+ * another above (the matrix cores over 32-wide steps of exact bf16 parts), so a token's route weights, and
+ * rarely its output bits, can change when a batch crosses M = 64 / 65. With MOE_FLAG_BATCH_INVARIANT the
+ * router takes its matrix-core kernel at every M (at decode widths a few microseconds slower, and through the
+ * separate selection and permutation kernels): a token's ids, route weights and outputs are then the same bits
+ * in every batch. Unknown flag bits are refused (MOE_ERR_INVALID_ARG). */
+#define MOE_FLAG_BATCH_INVARIANT 1u
 
 /* Routed experts in packed MXFP4 (section 1 table, section 2 formats). Host struct of device pointers. */
 typedef struct {

@@ -22,7 +22,7 @@ __all__ = [
     "moe_mxfp4_stage_scales_bytes", "moe_prepare_mxfp4_scales", "moe_expert_ffn_f32", "moe_shared_expert_f32",
     "moe_combine_sum_f32", "moe_combine_official_f32", "moe_fp8_linear_workspace_bytes", "moe_fp8_linear",
     "moe_mxfp4_tiled_weights_bytes", "moe_prepare_mxfp4_weights", "moe_fp8_tiled_weights_bytes",
-    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "TILED_ROWS_PER_EXPERT",
+    "moe_prepare_fp8_weights", "moe_fp8_linear_tiled", "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "TILED_ROWS_PER_EXPERT", "FLAG_BATCH_INVARIANT",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
@@ -41,7 +41,7 @@ class MoeError(RuntimeError):
 
 class _Dims(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float)]
+                ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
 class _MXFP4(ctypes.Structure):
@@ -125,9 +125,10 @@ class Dims:
     inter: int
     top_k: int
     route_scale: float = 1.5
+    flags: int = 0   # MOE_FLAG_* bits (FLAG_BATCH_INVARIANT)
 
     def c(self) -> _Dims:
-        return _Dims(self.num_experts, self.hidden, self.inter, self.top_k, self.route_scale)
+        return _Dims(self.num_experts, self.hidden, self.inter, self.top_k, self.route_scale, self.flags)
 
 
 @dataclass
@@ -341,6 +342,9 @@ def moe_forward(dims: Dims, x, gate_w, gate_b, packed: MXFP4Experts | None, deco
 
 # size of the library-owned workspace of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES in moe.h)
 NOALLOC_SCRATCH_BYTES = 16 << 20
+# Dims.flags bit: one router summation order at every M, so a token's bits do not depend on the batch
+# (MOE_FLAG_BATCH_INVARIANT)
+FLAG_BATCH_INVARIANT = 1
 # the routed GEMMs run over the row-tile list once M * top_k >= TILED_ROWS_PER_EXPERT * num_experts
 # (MOE_TILED_ROWS_PER_EXPERT in moe.h)
 TILED_ROWS_PER_EXPERT = 6

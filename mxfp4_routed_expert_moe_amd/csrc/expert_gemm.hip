@@ -480,7 +480,10 @@ size_t stream_lds_bytes(int K, int rows) {
 
 // Rows per pass: a function of (M, k, E) only, so launch geometry never depends on routed data. The per-row
 // arithmetic (the same MFMAs over the same K steps) does not depend on it, so outputs are identical either way.
+// The 8-row staging is used only while it fits 64 KB of LDS (K up to about 6,000; the contract's H = 5120 takes
+// 56.7 KB); larger K keeps 4 rows.
 static int stream_rows(const GemmProblem& p) {
+  if (stream_lds_bytes(p.K, kStreamRowsMany) > 65536) return kStreamRowsFew;
   if (p.dense) return p.M > kStreamRowsFew ? kStreamRowsMany : kStreamRowsFew;
   return (long long)p.M * p.k >= 3LL * p.num_experts ? kStreamRowsMany : kStreamRowsFew;
 }

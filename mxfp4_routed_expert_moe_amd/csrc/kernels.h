@@ -16,16 +16,17 @@ namespace moe {
 // the per-32 E4M3 QDQ of x, and the selection may run fused with the permutation.
 constexpr int kRouterSmallM = 64;
 // fp32 logits of the raw bf16 activations against the fp32 gate weight [E, H], as
-// router_logit_parts(M, H) partial planes [parts, M, E] (summed in order by the select kernel).
-// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise).
-int router_logit_parts(int M, int H);
+// router_logit_parts(M, H, mfma_order) partial planes [parts, M, E] (summed in order by the select kernel).
+// At M <= kRouterSmallM it also writes x_q / x_s (ignored otherwise). mfma_order: the matrix-core kernel (and its
+// summation order) at every M, the decode widths included; then the selection QDQs x.
+int router_logit_parts(int M, int H, bool mfma_order = false);
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, hipStream_t s);
-// sqrt(softplus) scores, biased top-k, normalised route weights; at M > kRouterSmallM also the
-// per-32 E4M3 QDQ of x.
+                          uint8_t* x_q, uint8_t* x_s, bool mfma_order, hipStream_t s);
+// sqrt(softplus) scores, biased top-k, normalised route weights; at M > kRouterSmallM, or with mfma_order, also
+// the per-32 E4M3 QDQ of x.
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
-                              uint8_t* x_q, uint8_t* x_s, hipStream_t s);
+                              uint8_t* x_q, uint8_t* x_s, bool mfma_order, hipStream_t s);
 
 // ---- permutation (permute.hip) -------------------------------------------------------------
 // Stable counting sort of the M*k (token, slot) pairs by expert id.

@@ -32,6 +32,9 @@ struct WsLayout {
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Batch-invariant mode: the router runs its matrix-core kernel (one summation order) at every M.
+inline bool batch_invariant(const moe_dims* d) { return (d->flags & MOE_FLAG_BATCH_INVARIANT) != 0u; }
+
 WsLayout ws_layout(const moe_dims* d, int64_t M) {
   WsLayout L{};
   size_t off = 0;
@@ -84,6 +87,7 @@ moe_status check_dims(const moe_dims* d, int32_t M) {
   if (d == nullptr || M < 0) return MOE_ERR_INVALID_ARG;
   const int E = d->num_experts, H = d->hidden, I = d->inter, k = d->top_k;
   if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || !std::isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
+  if ((d->flags & ~MOE_FLAG_BATCH_INVARIANT) != 0u) return MOE_ERR_INVALID_ARG;
   if (E > 256 || k > 8 || k > E) return MOE_ERR_UNSUPPORTED;
   if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (H > 8192 || I > 8192) return MOE_ERR_UNSUPPORTED;   // decode-width LDS staging stays within 64 KB
@@ -192,9 +196,9 @@ void do_route(const moe_dims* d, int M, const uint16_t* x, const float* gw, cons
               float* rw, uint8_t* xq, uint8_t* xs, void* ws, hipStream_t s) {
   const WsLayout L = ws_layout(d, M);
   float* logits = at<float>(ws, L.logits);
-  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, xq, xs, s);
+  moe::launch_router_logits(M, d->hidden, d->num_experts, x, gw, logits, xq, xs, batch_invariant(d), s);
   moe::launch_router_select_qdq(M, d->hidden, d->num_experts, d->top_k, d->route_scale, logits, gb, x, ids, rw, xq,
-                                xs, s);
+                                xs, batch_invariant(d), s);
 }
 
 // GEMM1: I rows of w1 and w3 over H inputs; activation row = token of the pair; output h rows at
@@ -372,9 +376,10 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* pairs = at<int32_t>(ws, L.pairs);
   int32_t* active = at<int32_t>(ws, L.active);
-  if (M <= moe::kRouterSmallM) {   // decode widths: logits + QDQ, then selection and permutation in one block
+  const bool fused = M <= moe::kRouterSmallM && !batch_invariant(dims);
+  if (fused) {   // decode widths: logits + QDQ, then selection and permutation in one block
     float* logits = at<float>(ws, L.logits);
-    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, s);
+    moe::launch_router_logits(M, dims->hidden, dims->num_experts, x, gate_w, logits, xq, xs, false, s);
     moe::launch_select_permute_small(M, dims->hidden, dims->num_experts, dims->top_k, dims->route_scale, logits,
                                      gate_b, ids, rw, at<int32_t>(ws, L.counts), offsets, pairs,
                                      at<int32_t>(ws, L.inv), active, at<int32_t>(ws, L.out_rows), s);
@@ -386,7 +391,7 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   // decode widths on the decode-width kernels: each token's slot rows are written in ascending expert-id order
   // (rows from the selection kernel), so the combine reads no ids
-  const bool ranked = M <= moe::kRouterSmallM && !routed_tiled(dims, M);
+  const bool ranked = fused && !routed_tiled(dims, M);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
                 at<uint8_t>(ws, L.h_s), true, ws, s, ranked ? at<int32_t>(ws, L.out_rows) : nullptr);
   uint16_t* sh_out = nullptr;

@@ -211,11 +211,11 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
     }
 }
 
-// One wave per token, four tokens per block: scores, biased top-k, normalisation; at M > 64 the wave
-// also QDQs the token's row (one 32-wide block per lane per pass); at M <= 64 the logits kernel has.
+// One wave per token, four tokens per block: scores, biased top-k, normalisation; with qdq the wave also
+// QDQs the token's row (one 32-wide block per lane per pass); otherwise the logits kernel has.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, int k, float route_scale,
-                                                         int nparts, const float* __restrict__ logits,
+                                                         int nparts, int qdq, const float* __restrict__ logits,
                                                          const float* __restrict__ gate_b,
                                                          const uint16_t* __restrict__ x,
                                                          int32_t* __restrict__ ids, float* __restrict__ rw,
@@ -223,17 +223,19 @@ __global__ __launch_bounds__(256) void router_select_qdq(int M, int H, int E, in
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= M) return;
   select_token<NJ>(t, M, E, k, route_scale, nparts, logits, gate_b, lane, ids, rw, nullptr, nullptr);
-  if (M <= kSmallM) return;
+  if (!qdq) return;
   const int nb = H / 32;
   for (int b = lane; b < nb; b += 64)
     qdq_block32(x + (size_t)t * H + b * 32, x_q + (size_t)t * H + b * 32, x_s + (size_t)t * nb + b);
 }
 
-int router_logit_parts(int M, int H) { return M <= kSmallM ? (H + kChunkH - 1) / kChunkH : kLargeParts; }
+int router_logit_parts(int M, int H, bool mfma_order) {
+  return (M <= kSmallM && !mfma_order) ? (H + kChunkH - 1) / kChunkH : kLargeParts;
+}
 
 void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* gate_w, float* logits,
-                          uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  if (M <= kSmallM) {
+                          uint8_t* x_q, uint8_t* x_s, bool mfma_order, hipStream_t s) {
+  if (M <= kSmallM && !mfma_order) {
     router_logits_small<<<dim3((E + 3) / 4, router_logit_parts(M, H)), dim3(256), 0, s>>>(M, H, E, x, gate_w, logits,
                                                                                            x_q, x_s);
   } else {
@@ -244,14 +246,15 @@ void launch_router_logits(int M, int H, int E, const uint16_t* x, const float* g
 
 void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, const float* logits,
                               const float* gate_b, const uint16_t* x, int32_t* ids, float* rw,
-                              uint8_t* x_q, uint8_t* x_s, hipStream_t s) {
-  const int parts = router_logit_parts(M, H);
+                              uint8_t* x_q, uint8_t* x_s, bool mfma_order, hipStream_t s) {
+  const int parts = router_logit_parts(M, H, mfma_order);
+  const int qdq = (M > kSmallM || mfma_order) ? 1 : 0;   // at decode widths the small logits kernel QDQs x
   if (E <= 128)
-    router_select_qdq<2><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, logits, gate_b, x, ids,
-                                                                 rw, x_q, x_s);
+    router_select_qdq<2><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, qdq, logits, gate_b,
+                                                                 x, ids, rw, x_q, x_s);
   else
-    router_select_qdq<4><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, logits, gate_b, x, ids,
-                                                                 rw, x_q, x_s);
+    router_select_qdq<4><<<dim3((M + 3) / 4), dim3(256), 0, s>>>(M, H, E, k, route_scale, parts, qdq, logits, gate_b,
+                                                                 x, ids, rw, x_q, x_s);
 }
 
 }  // namespace moe

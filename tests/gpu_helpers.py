@@ -22,9 +22,9 @@ def upload(inp: dict) -> dict:
     return {k: dev_tensor(v) for k, v in inp.items() if isinstance(v, np.ndarray) and k not in ("hot_rows", "hot_experts")}
 
 
-def dims_of(cfg):
+def dims_of(cfg, flags=0):
     import mxfp4_routed_expert_moe_amd as m
-    return m.Dims(cfg.E, cfg.H, cfg.I, cfg.k, cfg.route_scale)
+    return m.Dims(cfg.E, cfg.H, cfg.I, cfg.k, cfg.route_scale, flags)
 
 
 def packed_of(d: dict):
@@ -55,12 +55,12 @@ def tiled_of(cfg, d: dict):
     return m.MXFP4Experts(None, d["s1"], None, d["s3"], None, d["s2"], stage_scales=st, tiled_weights=tw)
 
 
-def forward(cfg, d: dict, decoded=None, with_shared=True, M=None, packed=None):
+def forward(cfg, d: dict, decoded=None, with_shared=True, M=None, packed=None, flags=0):
     """Run moe_forward; returns dict of host arrays (out, ids, rw, shared_out). packed: another form of the
-    routed experts (e.g. tiled_of) instead of the row-major one."""
+    routed experts (e.g. tiled_of) instead of the row-major one; flags: moe_dims flags."""
     import mxfp4_routed_expert_moe_amd as m
     M = cfg.M if M is None else M
-    dims = dims_of(cfg)
+    dims = dims_of(cfg, flags)
     ws = m.workspace(dims, M)
     out = torch.empty((M, cfg.H), dtype=torch.int16, device="cuda")
     ids = torch.empty((M, cfg.k), dtype=torch.int32, device="cuda")
@@ -70,7 +70,8 @@ def forward(cfg, d: dict, decoded=None, with_shared=True, M=None, packed=None):
     pk = None if decoded is not None else (packed if packed is not None else packed_of(d))
     m.moe_forward(dims, d["x"][:M], d["gate_w"], d["gate_b"], pk, decoded, sh, out, ids, rw, sh_out, ws)
     torch.cuda.synchronize()
-    res = dict(out=bf16_host(out), ids=ids.cpu().numpy(), rw=rw.cpu().numpy(), out_bits=out.cpu().numpy())
+    res = dict(out=bf16_host(out), ids=ids.cpu().numpy(), rw=rw.cpu().numpy(), out_bits=out.cpu().numpy(),
+               rw_bits=rw.cpu().numpy().view(np.uint32))
     if sh_out is not None:
         res["shared_out"] = bf16_host(sh_out)
     return res

@@ -32,7 +32,7 @@ def lib():
 
 class Dims(ctypes.Structure):
     _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float)]
+                ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
 class Six(ctypes.Structure):
@@ -288,7 +288,19 @@ def test_binding_constants_match_the_header():
     import mxfp4_routed_expert_moe_amd as m
     text = open(HEADER).read()
     scratch = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    flag = re.search(r"#define MOE_FLAG_BATCH_INVARIANT (\d+)u", text)
+    assert flag and m.FLAG_BATCH_INVARIANT == int(flag.group(1))
     tiled = re.search(r"#define MOE_TILED_ROWS_PER_EXPERT (\d+)", text)
     assert scratch and tiled
     assert m.NOALLOC_SCRATCH_BYTES == int(scratch.group(1)) << int(scratch.group(2))
     assert m.TILED_ROWS_PER_EXPERT == int(tiled.group(1))
+
+
+def test_unknown_dims_flags_are_refused(lib):
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_workspace_bytes.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+    ok = Dims(128, 5120, 2304, 6, 1.5, 1)   # MOE_FLAG_BATCH_INVARIANT
+    assert lib.moe_workspace_bytes(ctypes.byref(ok), 8192) > 0
+    for flags in (2, 4, 0x80000000, 3):
+        assert lib.moe_workspace_bytes(ctypes.byref(Dims(128, 5120, 2304, 6, 1.5, flags)), 64) == 0
+        assert _forward(lib, Dims(128, 5120, 2304, 6, 1.5, flags), 8) == INVALID

@@ -131,11 +131,18 @@ def test_qdq_codes_exhaustive_over_bf16():
 
 
 @pytest.mark.parametrize("M,k,E,skew", [(8192, 6, 128, False), (37, 6, 128, False), (64, 6, 128, True),
-                                        (4, 2, 8, False), (1, 8, 256, False)])
+                                        (4, 2, 8, False), (1, 8, 256, False), (2048, 6, 256, "sparse"),
+                                        (4096, 4, 64, False), (3000, 6, 128, True)])
 def test_permute_is_bit_exact(M, k, E, skew):
+    """Counts, offsets, pairs, inverse and the active list, bit for bit against the oracle's counting sort;
+    the multi-block kernel (more than 1024 pairs) with every expert, with a sparse set of experts (gaps in
+    the active list) and with all tokens on the same k experts."""
     rng = np.random.default_rng(M + E)
-    if skew:
+    if skew is True:
         ids = np.tile(np.arange(k, dtype=np.int32)[::-1], (M, 1))
+    elif skew == "sparse":
+        pool = np.sort(rng.choice(E, size=41, replace=False))
+        ids = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(M)]).astype(np.int32)
     else:
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(M)]).astype(np.int32)
     dims = m().Dims(E, 256, 128, k)
@@ -540,6 +547,42 @@ def test_decode_path_is_batch_invariant():
     for M in (32, 64):
         assert np.array_equal(outs[M][0], outs[8][0]), f"routing of the first tokens changes with M={M}"
         assert np.array_equal(outs[M][1], outs[8][1]), f"outputs of the first tokens change with M={M}"
+
+
+def test_batch_invariant_mode_across_the_switches():
+    """With MOE_FLAG_BATCH_INVARIANT a token's ids, route weights and output are the same bits in every batch,
+    across the router switch (M = 64 / 65) and the streamed / row-tiled GEMM switch (M = 127 / 128 at E = 128,
+    k = 6): the first 16 tokens alone and in batches of 64, 65, 127, 128 and 300 (full-size layer); the batch of
+    65 against its first 64 tokens, 300 against its first 128. The flagged router (the matrix-core kernel at
+    every M) is the default one above 64 tokens, bit for bit, and within tolerance of the oracle below."""
+    cfg, inp, d = cfg_inputs(2, M=300)
+    inv = m().FLAG_BATCH_INVARIANT
+    runs = {M: forward(cfg, d, M=M, flags=inv) for M in (16, 64, 65, 127, 128, 300)}
+    base = runs[16]
+    for M, r in runs.items():
+        assert np.array_equal(r["ids"][:16], base["ids"]), f"ids of the first tokens change at M={M}"
+        assert np.array_equal(r["rw_bits"][:16], base["rw_bits"]), f"route weights of the first tokens change at M={M}"
+        assert np.array_equal(r["out_bits"][:16], base["out_bits"]), f"outputs of the first tokens change at M={M}"
+    assert np.array_equal(runs[65]["out_bits"][:64], runs[64]["out_bits"])
+    assert np.array_equal(runs[300]["out_bits"][:128], runs[128]["out_bits"])
+    # above 64 tokens the flag changes nothing
+    plain300 = forward(cfg, d, M=300)
+    assert np.array_equal(plain300["out_bits"], runs[300]["out_bits"])
+    assert np.array_equal(plain300["rw_bits"], runs[300]["rw_bits"])
+    # below, the flagged router against the oracle and against the default (decode-width) router
+    ref = O.moe_forward(inp, cfg, tokens=list(range(16)))
+    sub = synth.get_config(2, M=16)
+    diff = check_routing(base["ids"], base["rw"], ref["route"], sub)
+    if diff.size:
+        ref = O.moe_forward(inp, cfg, tokens=list(range(16)), ids=base["ids"], rw=base["rw"])
+    assert_within(base["out"], ref["out"], "batch-invariant router at M = 16")
+    plain64 = forward(cfg, d, M=64)
+    same = np.all(plain64["ids"] == runs[64]["ids"], axis=1)   # (a near-tie may select differently)
+    moved = np.mean(plain64["rw_bits"][same] != runs[64]["rw_bits"][same])
+    rel = np.abs(plain64["rw"][same].astype(np.float64) - runs[64]["rw"][same]) / np.abs(runs[64]["rw"][same])
+    print(f"M = 64: the default router's route weights differ from the batch-invariant ones on {moved:.4f} "
+          f"(max {rel.max():.3g} relative); outputs bit-equal on {np.mean(plain64['out_bits'] == runs[64]['out_bits']):.5f}")
+    assert rel.max() <= 8 * 2.0 ** -23
 
 
 @pytest.mark.parametrize("M", [1, 8, 63, 64, 65])
