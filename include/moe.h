@@ -80,9 +80,10 @@ typedef struct {
  * sums its fp32 logits in one order up to M = 64 tokens (512-wide chunks, 64 lanes' 8-term FMA chains) and in
  * another above (the matrix cores over 32-wide steps of exact bf16 parts), so a token's route weights, and
  * rarely its output bits, can change when a batch crosses M = 64 / 65. With MOE_FLAG_BATCH_INVARIANT the
- * router takes its matrix-core kernel at every M (at decode widths a few microseconds slower, and through the
- * separate selection and permutation kernels): a token's ids, route weights and outputs are then the same bits
- * in every batch. Unknown flag bits are refused (MOE_ERR_INVALID_ARG). */
+ * router takes its matrix-core kernel at every M (at decode widths slower: about 33 us more at M = 8 on the
+ * full-size layer, through the separate selection and permutation kernels): a token's ids, route weights and
+ * outputs are then the same bits in every batch. Above 64 tokens the flag changes nothing. Unknown flag bits
+ * are refused (MOE_ERR_INVALID_ARG). */
 #define MOE_FLAG_BATCH_INVARIANT 1u
 
 /* Routed experts in packed MXFP4 (section 1 table, section 2 formats). Host struct of device pointers. */

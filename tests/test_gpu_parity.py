@@ -704,3 +704,36 @@ def test_full_size_layer_with_tiled_weights_is_identical(M):
     m().moe_forward(dims, d["x"][:M], d["gate_w"], d["gate_b"], pk, None, None, out, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), a["out_bits"])
+
+
+def _random_shapes(n=8, seed=2026):
+    """Seeded layer shapes across the supported domain: E, k, H, I, M, shared expert, both kernel families."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        E = int(rng.choice([8, 16, 24, 64, 128, 256]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        H = 128 * int(rng.integers(1, 9))
+        I = 128 * int(rng.integers(1, 7))
+        M = int(rng.choice([1, 3, 17, 50, 130, 300]))
+        shapes.append(dict(M=M, H=H, I=I, E=E, k=k, shared=bool(rng.integers(0, 2))))
+    return shapes
+
+
+@pytest.mark.parametrize("over", _random_shapes(), ids=lambda o: "M{M}_H{H}_I{I}_E{E}_k{k}".format(**o))
+def test_random_shapes_match_oracle(over):
+    """Seeded random shapes (experts 8 .. 256, top-k 1 .. 8, H and I from 128 up, batch 1 .. 300, with and
+    without the shared expert): every token within tolerance of the oracle, through whichever router path and
+    GEMM family the shape selects."""
+    cfg, inp, d = cfg_inputs(0, **over)
+    res, ref, diff = _check_forward(cfg, inp, d)
+    if cfg.shared:
+        assert_within(res["shared_out"], ref["shared_y"], "shared expert")
+
+
+def test_long_inner_dimension_keeps_four_row_passes():
+    """H = 8192: the 8-row decode staging would not fit 64 KB of LDS, so the w1/w3 pass keeps 4 rows while the
+    w2 pass (K = I) takes 8; every token against the oracle."""
+    cfg, inp, d = cfg_inputs(0, M=20, H=8192, I=256, E=8, k=2)
+    assert 3 * cfg.E <= cfg.M * cfg.k < m().TILED_ROWS_PER_EXPERT * cfg.E
+    _check_forward(cfg, inp, d)
