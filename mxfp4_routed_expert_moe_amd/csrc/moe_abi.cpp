@@ -365,9 +365,44 @@ moe_status check_forward(const moe_dims* dims, int32_t M, const uint16_t* x, con
 
 // The whole layer on a validated workspace of ws_layout(dims, M).total bytes. No kernel relies on the
 // workspace's previous contents: every buffer is written before it is read within the call.
+// ---- the shared expert beside the routed experts ---------------------------------------------------
+// At prefill widths the FP8 shared expert (288 / 320 blocks of its two GEMMs at M = 2048, a second wave of blocks
+// that fills a ninth of the chip) runs on a second stream of the same device, forked from the caller's stream
+// after the router and joined before the combine, so its blocks fill the CUs the routed GEMMs leave idle. One
+// such stream and two events per device, created on first use and kept; the fork / join sequence of a call is
+// enqueued under a lock, so calls from several host threads pair their own records and waits. (Graph capture:
+// the fork event brings the second stream into the caller's capture and the join returns it.)
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// The device's side stream (nullptr if it cannot be made: the shared expert then runs on the caller's stream).
+// Called with g_side_mu held.
+SideStream* side_stream_locked() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr && !ss.failed) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  return ss.failed ? nullptr : &ss;
+}
+
 void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const float* gate_w, const float* gate_b,
                   const moe_mxfp4_experts* packed, const moe_bf16_experts* decoded, const moe_fp8_expert* shared,
-                  uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws, hipStream_t s) {
+                  uint16_t* out, int32_t* ids_out, float* rw_out, uint16_t* shared_out, void* ws, hipStream_t s,
+                  bool side_ok = true) {
   const WsLayout L = ws_layout(dims, M);
   int32_t* ids = ids_out ? ids_out : at<int32_t>(ws, L.ids);
   float* rw = rw_out ? rw_out : at<float>(ws, L.rw);
@@ -389,14 +424,33 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
                         at<int32_t>(ws, L.inv), active, s);
   }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
+  uint16_t* sh_out = shared != nullptr ? (shared_out ? shared_out : at<uint16_t>(ws, L.sh_out)) : nullptr;
+  // the shared expert on the device's second stream (prefill widths), else after the routed experts
+  std::unique_lock<std::mutex> side_lock;
+  SideStream* side = nullptr;
+  if (shared != nullptr && side_ok && shared_mfma(M)) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mu);
+    side = side_stream_locked();
+    if (side != nullptr && (hipEventRecord(side->fork, s) != hipSuccess ||
+                            hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)) {
+      (void)hipGetLastError();
+      side = nullptr;
+    }
+    if (side != nullptr) {
+      do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr,
+                side->stream);
+      (void)hipEventRecord(side->join, side->stream);
+    }
+  }
   // decode widths on the decode-width kernels: each token's slot rows are written in ascending expert-id order
   // (rows from the selection kernel), so the combine reads no ids
   const bool ranked = fused && !routed_tiled(dims, M);
   do_expert_ffn(dims, M, xq, xs, packed, decoded, rw, offsets, pairs, active, slot, nullptr, at<uint8_t>(ws, L.h_q),
                 at<uint8_t>(ws, L.h_s), true, ws, s, ranked ? at<int32_t>(ws, L.out_rows) : nullptr);
-  uint16_t* sh_out = nullptr;
-  if (shared != nullptr) {
-    sh_out = shared_out ? shared_out : at<uint16_t>(ws, L.sh_out);
+  if (side != nullptr) {
+    (void)hipStreamWaitEvent(s, side->join, 0);
+    side_lock.unlock();
+  } else if (shared != nullptr) {
     do_shared(dims, M, xq, xs, shared, at<uint8_t>(ws, L.sh_q), at<uint8_t>(ws, L.sh_s), sh_out, nullptr, s);
   }
   moe::launch_combine(M, dims->hidden, dims->top_k, ranked ? nullptr : ids, slot, sh_out, out, s);
@@ -586,7 +640,8 @@ moe_status moe_forward_noalloc(const moe_dims* dims, int32_t M, const uint16_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* ws = nullptr;
   MOE_TRY(scratch_for_stream(s, &ws));
-  forward_impl(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out, ws, s);
+  // (no second stream here: creating it would allocate)
+  forward_impl(dims, M, x, gate_w, gate_b, packed, decoded, shared, out, ids_out, rw_out, shared_out, ws, s, false);
   return launched();
 }
 
