@@ -318,6 +318,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
     uint8_t* sst = lds + kTM * 256;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
+      if (b >= nbv) continue;   // (wave-uniform) 16-row groups past the tile's rows: nothing to compute or store
       const int t = 16 * b + r16;
       const float rwv = t < nrows ? *reinterpret_cast<const float*>(&lds[kOffRw + 4 * t]) : 1.0f;
 #pragma unroll
@@ -386,6 +387,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
     // (512 columns) per wave instruction
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
+      if (b >= nbv) continue;   // (wave-uniform) 16-row groups past the tile's rows are never stored
       const int t = 16 * b + r16;
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
