@@ -216,13 +216,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_bf16(GemmProblem p, const 
       float amax = 0.0f;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float gv = round_bf16(acc[half][b][v]);
-          const float uv = round_bf16(acc[2 + half][b][v]);
-          h[half][v] = round_bf16(swiglu(gv, uv, rwv, true));
-          amax = fmaxf(amax, fabsf(h[half][v]));
-        }
+        amax = fmaxf(amax, swiglu_bf16x4(acc[half][b], acc[2 + half][b], rwv, true, h[half]));
       // the 32 columns of this QDQ block for row r16 live in lanes r16 + 16 g, g = 0..3
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));

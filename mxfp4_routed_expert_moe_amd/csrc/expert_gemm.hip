@@ -153,13 +153,7 @@ __global__ __launch_bounds__(256) void expert_gemm_small(GemmProblem p) {
         float amax = 0.0f;
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float gv = round_bf16(sum[half][v]);
-            const float uv = round_bf16(sum[2 + half][v]);
-            h[half][v] = round_bf16(swiglu(gv, uv, rwv, !p.dense));
-            amax = fmaxf(amax, fabsf(h[half][v]));
-          }
+          amax = fmaxf(amax, swiglu_bf16x4(sum[half], sum[2 + half], rwv, !p.dense, h[half]));
         // the 32 rows of this QDQ block for token column r16 live in lanes r16 + 16 g, g = 0..3
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
@@ -435,12 +429,7 @@ __global__ __launch_bounds__(256) void expert_gemm_stream(GemmProblem p) {
         const f32x4 gf = xch[wave * 64 + lane], uf = xch[(wave + 2) * 64 + lane];
         float rwv = 1.0f;
         if (valid && !p.dense) rwv = p.rw[p.pairs[pos]];
-        float amax = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          h[v] = round_bf16(swiglu(round_bf16(gf[v]), round_bf16(uf[v]), rwv, !p.dense));
-          amax = fmaxf(amax, fabsf(h[v]));
-        }
+        float amax = swiglu_bf16x4(gf, uf, rwv, !p.dense, h);
         // this wave's 16 columns of row r16 live in lanes r16 + 16 g, g = 0..3
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));

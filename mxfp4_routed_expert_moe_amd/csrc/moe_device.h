@@ -31,6 +31,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_
 // fp32 -> the bf16 value it rounds to, as an fp32
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16_rne(f)); }
 
+// Two values rounded to bf16 (round to nearest even) and back to fp32 with one packed conversion
+// (v_cvt_pk_bf16_f32): the same bits as round_bf16 on each.
+__device__ __forceinline__ void round_bf16x2(float& a, float& b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  a = bits_to_f32(pk << 16);
+  b = bits_to_f32(pk & 0xFFFF0000u);
+}
+
 // E8M0 byte -> fp32 scale 2^(b-127); bytes 1..254 are exact normal fp32 values
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return bits_to_f32((b & 0xFFu) << 23); }
 
@@ -93,10 +103,10 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed8, float scal
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// e^x in fp32 as 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32, 1 ulp). The product
-// x log2 e is carried as hi + lo: hi = fp32(x * L2E_HI), lo = the exact error of that product (an FMA)
-// plus x * L2E_LO, where L2E_HI + L2E_LO is log2 e to twice fp32 precision (a Cody-Waite split); then
-// e^x = 2^hi (1 + lo ln 2). Overflow (x above ln FLT_MAX) returns +inf.
+// e^x in fp32 for x <= 80 as 2^(x log2 e) on the hardware base-2 exponential (v_exp_f32, 1 ulp). The
+// product x log2 e is carried as hi + lo: hi = fp32(x * L2E_HI), lo = the exact error of that product (an
+// FMA) plus x * L2E_LO, where L2E_HI + L2E_LO is log2 e to twice fp32 precision (a Cody-Waite split); then
+// e^x = 2^hi (1 + lo ln 2). (No overflow guard: the caller keeps x at most 80, e^80 < 2^116.)
 __device__ __forceinline__ float exp_f32(float x) {
   constexpr float kL2eHi = 1.44269502162933349609375f;   // fp32(log2 e)
   constexpr float kL2eLo = 1.9259629911266175e-8f;       // log2 e - kL2eHi
@@ -104,28 +114,47 @@ __device__ __forceinline__ float exp_f32(float x) {
   const float hi = x * kL2eHi;
   const float lo = fmaf(x, kL2eLo, fmaf(x, kL2eHi, -hi));
   const float p = __builtin_amdgcn_exp2f(hi);
-  return x > 88.72f ? __builtin_inff() : fmaf(p, lo * kLn2, p);
+  return fmaf(p, lo * kLn2, p);
 }
 
-// g / d for d >= 1 or d = +inf: hardware reciprocal (1 ulp), then one FMA correction of the quotient
-// from its exact residual g - d q.
+// g / d for finite d >= 1: hardware reciprocal (1 ulp), then one FMA correction of the quotient from its
+// exact residual g - d q.
 __device__ __forceinline__ float div_by_ge1(float g, float d) {
   const float r = __builtin_amdgcn_rcpf(d);
   const float q = g * r;
-  const float q2 = fmaf(fmaf(-d, q, g), r, q);
-  return d == __builtin_inff() ? g * 0.0f : q2;
+  return fmaf(fmaf(-d, q, g), r, q);
 }
 
 // SwiGLU of the routed/shared expert (section 2 "Expert", section 4 math): g and u are the
 // bf16-rounded linear outputs; u is clamped to [-10, 10] and g to at most 10; then
 // h = (g / (1 + exp(-g))) * u in fp32, times the route weight rw (1 for the shared expert).
+// g is also held at -80 from below, which keeps e^-g finite (one v_med3 instead of overflow guards): below
+// -80 the exact |h| is under 80 e^-80 * 10 * rw < 1.5e-32 * rw and the computed one (silu(-80) * u * rw)
+// too, both far under the 2^-32 below which the QDQ that follows makes every value a zero code of h's
+// sign (its scale is at least 2^-22), and both have the sign of -u * rw: the codes are the same.
 __device__ __forceinline__ float swiglu(float g, float u, float rw, bool weighted) {
-  g = fminf(g, 10.0f);
+  g = fminf(fmaxf(g, -80.0f), 10.0f);
   u = fminf(fmaxf(u, -10.0f), 10.0f);
   const float d = 1.0f + exp_f32(-g);
   float h = div_by_ge1(g, d) * u;
   if (weighted) h = rw * h;
   return h;
+}
+
+// The SwiGLU step of an epilogue for four (g, u) accumulator pairs of a lane (any type indexable 0..3): g
+// and u rounded to bf16 as pairs, swiglu, h rounded to bf16 two at a time. Writes h[0..3] and returns the
+// largest |h| of the four.
+template <class V>
+__device__ __forceinline__ float swiglu_bf16x4(const V& ga, const V& ua, float rw, bool weighted, float* h) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float gv = ga[v], uv = ua[v];
+    round_bf16x2(gv, uv);
+    h[v] = swiglu(gv, uv, rw, weighted);
+  }
+  round_bf16x2(h[0], h[1]);
+  round_bf16x2(h[2], h[3]);
+  return fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
 }
 
 }  // namespace moe
