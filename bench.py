@@ -42,8 +42,8 @@ WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m81
 # were measured on (sha256 prefix); after any change to it the traffic is reported as null until re-measured.
 FETCH_SCALE, WRITE_SCALE = 1048576 / 524300.9, 1.0
 MEASURED_TRAFFIC = {
-    "decode_m8": dict(src="expert_gemm.hip", sha="074a87afeb08f108", fetch_kib=227870.5, write_kib=135.1),
-    "prefill_m8192": dict(src="expert_wide.hip", sha="0068fe82265a2b5c", fetch_kib=1498531.8, write_kib=114387.0),
+    "decode_m8": dict(src="expert_gemm.hip", sha="9d186bd42894c2f5", fetch_kib=227911.2, write_kib=135.1),
+    "prefill_m8192": dict(src="expert_wide.hip", sha="ad57f8a5cc8577ce", fetch_kib=1507187.5, write_kib=114373.6),
 }
 
 
