@@ -47,6 +47,22 @@ MEASURED_TRAFFIC = {
 }
 
 
+# The fixed fp32 summation orders of the path (recorded so that routing and outputs are reproducible; the tie
+# flags of each run are in cpu_baseline.routing_ties).
+FP32_ORDERS = {
+    "router_logits": "M <= 64: per 512-wide chunk of H, 64 lanes x an 8-FMA chain then a butterfly over the lanes, "
+                     "chunks added in ascending order; M > 64 (and the batch-invariant flag): bf16 matrix cores over "
+                     "each quarter of H, three exact split-gate products per 32-wide step in ascending order, quarters "
+                     "added in ascending order",
+    "route_weights": "rw_j = (s_j / ((((s_0 + s_1) + ...) + s_{k-1}) + 1e-20)) * route_scale in fp32, slots in "
+                     "descending selection order, IEEE division",
+    "expert_dot_products": "each 128-wide K step's exact block products summed inside one block-scaled MFMA, the steps "
+                           "accumulated in fp32 in ascending order",
+    "combine": "acc = 0; acc += float(slot) over the token's experts in ascending expert id; then + float(shared); "
+               "out = bf16(acc)",
+}
+
+
 def _measured_traffic(workload: str):
     import hashlib
     m = MEASURED_TRAFFIC.get(workload)
@@ -915,6 +931,7 @@ def main():
         "roofline": r["roofline"],
         "telemetry": r["telemetry"],
         "inputs_sha256": r["inputs_sha256"],
+        "fp32_orders": FP32_ORDERS,
         "prefill": others.get("prefill_m8192"),
         "batched_decode_m64": others.get("batched_decode_m64"),
         "prefill_shared_skew_m2048": others.get("prefill_shared_skew_m2048"),
