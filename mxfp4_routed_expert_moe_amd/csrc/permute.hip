@@ -3,7 +3,8 @@
 // The expert GEMMs process the rows of one expert together (the grouped layout of the paper
 // "DeepSeek-V4-Flash on AMD gfx90a", section 7.1, and the route-direct chain of the page "DeepSeek V4 Flash REAP/XPU B70 Handoff"); the order inside an expert is
 // ascending pair id t*k + j, so results never depend on scheduling. No global atomics and no
-// in-kernel counter resets: block e counts with LDS atomics (integer, order-free) and compacts the
+// in-kernel counter resets: block e counts the pairs of expert e and of the experts below it with wave
+// ballots, finds its rank among the active experts from a presence mask of all ids, and compacts the
 // pairs of expert e with wave ballots.
 #include "kernels.h"
 #include "moe_device.h"
@@ -17,20 +18,20 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
                                                        int32_t* __restrict__ active) {
-  __shared__ int hist[256];
+  __shared__ unsigned long long present[4];   // bit x: some pair has expert id x (x < 256)
   __shared__ int wave_cnt[kPermWaves], wave_below[kPermWaves];
   __shared__ int base_off;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (e == 0)
-    for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+  if (tid < 4) present[tid] = 0ull;
   __syncthreads();
   // each wave owns a contiguous segment of the pair list (a multiple of 64 long). Block e counts the
-  // pairs of expert e and those of lower experts with wave ballots; only block 0 builds the full
-  // histogram (for the active list and the total).
+  // pairs of expert e and those of lower experts with wave ballots, and every block collects which ids
+  // occur (a 256-bit mask: its rank among the active experts and their number).
   const int seg = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;
   const int beg = wave * seg, end = min(P, beg + seg);
   int mine = 0, lower = 0;
+  unsigned long long pm0 = 0ull, pm1 = 0ull, pm2 = 0ull, pm3 = 0ull;
   constexpr int U = 8;   // ids in flight per lane
   for (int i0 = beg; i0 < end; i0 += 64 * U) {
     int v[U];
@@ -42,14 +43,30 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = v[u] >= 0 && v[u] < E;
-      if (e == 0 && ok) atomicAdd(&hist[v[u]], 1);
       mine += __popcll(__ballot(ok && v[u] == e));
       lower += __popcll(__ballot(ok && v[u] < e));
+      const unsigned long long bit = ok ? 1ull << (v[u] & 63) : 0ull;
+      const int q = v[u] >> 6;
+      pm0 |= q == 0 ? bit : 0ull;
+      pm1 |= q == 1 ? bit : 0ull;
+      pm2 |= q == 2 ? bit : 0ull;
+      pm3 |= q == 3 ? bit : 0ull;
     }
+  }
+  // OR of the presence words over the wave, then over the block (integer: order-free)
+  for (int off = 32; off >= 1; off >>= 1) {
+    pm0 |= __shfl_xor(pm0, off, 64);
+    pm1 |= __shfl_xor(pm1, off, 64);
+    pm2 |= __shfl_xor(pm2, off, 64);
+    pm3 |= __shfl_xor(pm3, off, 64);
   }
   if (lane == 0) {
     wave_cnt[wave] = mine;
     wave_below[wave] = lower;
+    atomicOr(&present[0], pm0);
+    atomicOr(&present[1], pm1);
+    atomicOr(&present[2], pm2);
+    atomicOr(&present[3], pm3);
   }
   __syncthreads();
   if (tid == 0) {
@@ -61,15 +78,17 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
     base_off = off;
     counts[e] = cnt;
     offsets[e] = off;
-    if (e == 0) {
-      int tot = 0, na = 0;
-      for (int j = 0; j < E; ++j) {
-        tot += hist[j];
-        if (hist[j] > 0) active[na++] = j;
-      }
-      for (int j = na; j < E; ++j) active[j] = -1;
-      offsets[E] = tot;
+    // rank of e among the active experts (ascending id), and their number
+    int rank = 0, n_active = 0;
+    for (int q = 0; q < 4; ++q) {
+      const unsigned long long m = present[q];
+      n_active += __popcll(m);
+      if (64 * q + 63 < e) rank += __popcll(m);
+      else if (64 * q <= e) rank += __popcll(m & ((1ull << (e & 63)) - 1ull));
     }
+    if (cnt > 0) active[rank] = e;   // positions < n_active
+    if (e >= n_active) active[e] = -1;   // padding: positions >= n_active, disjoint from the above
+    if (e == E - 1) offsets[E] = off + cnt;
   }
   __syncthreads();
   int base = base_off;
