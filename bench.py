@@ -9,9 +9,11 @@ Inputs are resident in HBM before the timed region starts. The expert weights ex
 step i uses replica i mod R, so the 256 MB last-level cache cannot serve them from a previous step.
 
 Printed: one JSON line. ``value`` is tokens/s of the M=8 decode-width layer (hidden 5120, 128 MXFP4
-experts, intermediate 2304, top-6) over the K timed steps. ``step_us`` holds the median, p10 and p90 of
-200 per-step HIP-event samples taken after a 0.5 s settle, ``telemetry`` the GPU clock, power and
-temperature polled meanwhile. ``roofline`` describes the dominant kernel, the grouped w1/w3 GEMM.
+experts, intermediate 2304, top-6) over the K timed steps. Without --warmup the timed steps follow 10 untimed
+ones and then 0.5 s more of untimed steps, so that the GPU's clocks have left their idle state (``warmup``
+reports all untimed steps). ``step_us`` holds the median, p10 and p90 of 200 per-step HIP-event samples taken
+after another 0.5 s of the layer running, ``telemetry`` the GPU clock, power and temperature polled
+meanwhile. ``roofline`` describes the dominant kernel, the grouped w1/w3 GEMM.
 ``prefill`` (8192 tokens), ``batched_decode_m64`` and ``prefill_shared_skew_m2048`` (2048 tokens with the FP8
 shared expert and 8 hot experts) hold the same figures for the other workloads, each with its layer's
 fractions of the HBM and MFMA peaks. ``peaks`` are this GPU's measured streaming-read and scaled-MFMA
@@ -330,11 +332,27 @@ def _percentiles(us):
                 p90=round(float(np.percentile(a, 90)), 2), min=round(float(a.min()), 2))
 
 
-def sample_steps(L: "Layer", n: int = 200, settle_s: float = 0.5) -> dict:
-    """After a 0.5 s settle, n steps each bracketed by its own pair of HIP events on the launch stream (the
-    weight replicas keep rotating): per-step microseconds as median, p10, p90."""
+def settle(L: "Layer", seconds: float, first: int = 0) -> int:
+    """Runs the layer back to back for at least `seconds` of wall time (untimed) and returns the steps run.
+    From idle the GPU's clocks take a few hundred milliseconds of load to reach their sustained state (the SMU
+    reports idle clocks when the load starts); measured on the decode layer, 100-step loops started from
+    idle run about 2 % slower than after 0.4 s of load."""
     import torch
-    time.sleep(settle_s)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            L.step(first + n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def sample_steps(L: "Layer", n: int = 200, settle_s: float = 0.5) -> dict:
+    """After a 0.5 s settle (the layer running back to back), n steps each bracketed by its own pair of HIP
+    events on the launch stream (the weight replicas keep rotating): per-step microseconds as median, p10,
+    p90."""
+    import torch
+    settle(L, settle_s)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i, (a, b) in enumerate(evs):
         a.record()
@@ -345,9 +363,11 @@ def sample_steps(L: "Layer", n: int = 200, settle_s: float = 0.5) -> dict:
 
 
 def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled: bool = True,
-            samples: int = 200) -> dict:
+            samples: int = 200, settle_s: float = 0.5) -> dict:
     """One workload: the timed K-step loop (whole-job rate), 200 event samples, graph replay, the split
-    entry points' kernel times, GEMM1 back to back (roofline timing) and clock / power telemetry."""
+    entry points' kernel times, GEMM1 back to back (roofline timing) and clock / power telemetry. The timed
+    loop follows `warmup` untimed steps and then, with settle_s > 0, settle_s seconds more of untimed steps
+    (the number of all untimed steps is returned as warmup_steps)."""
     import torch
 
     L = Layer(cid, replicas, tiled)
@@ -357,9 +377,10 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
         for i in range(warmup):
             L.step(i)
         torch.cuda.synchronize()
+        warmup_steps = warmup + (settle(L, settle_s, warmup) if settle_s > 0 else 0)
         t0 = time.perf_counter()
         for i in range(steps):
-            L.step(warmup + i)
+            L.step(warmup_steps + i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / steps
@@ -444,6 +465,7 @@ def measure(cid: int, steps: int, warmup: int, replicas: int, widths=None, tiled
         layer_flops += cfg.M * (f13 + f2)
     sec = ms * 1e-3
     res = dict(workload=cfg.name, M=cfg.M, ms_per_step=ms, tokens_per_s=cfg.M / sec, distinct_experts=D,
+               warmup_steps=warmup_steps, settle_s=settle_s,
                graph_ms_per_step=graph_ms, step_us=samp, kernel_us=kern_us,
                layer_algorithmic_bytes=layer_bytes, layer_algorithmic_flops=layer_flops,
                layer_hbm_frac=(layer_bytes / sec) / (HBM_PEAK_GBS * 1e9),
@@ -601,7 +623,8 @@ def leg(r: dict) -> dict:
                 kernel_us={k: round(v, 2) for k, v in r["kernel_us"].items()},
                 layer_hbm_frac=round(r["layer_hbm_frac"], 4), layer_mfma_frac=round(r["layer_mfma_frac"], 4),
                 layer_tflops=round(r["layer_tflops"], 1), roofline=r["roofline"], telemetry=r["telemetry"],
-                inputs_sha256=r["inputs_sha256"], weight_replicas=r["replicas"], weight_layout=r["weight_layout"])
+                inputs_sha256=r["inputs_sha256"], weight_replicas=r["replicas"], weight_layout=r["weight_layout"],
+                warmup_steps=r["warmup_steps"], warmup_settle_s=r["settle_s"])
 
 
 def measure_peaks() -> dict:
@@ -817,10 +840,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: 10, then the layer keeps running untimed "
+                         "until 0.5 s have passed, so that the clocks have left their idle state; an explicit "
+                         "value runs exactly that many)")
     ap.add_argument("--workload", default="decode_m8", choices=sorted(WORKLOADS))
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--samples", type=int, default=200, help="per-step HIP event samples after a 0.5 s settle")
+    ap.add_argument("--samples", type=int, default=200,
+                    help="per-step HIP event samples after a 0.5 s settle (the layer running back to back)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 8192-token prefill measurement")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the 64-token and 2048-token (shared expert, skewed routing) workloads")
@@ -838,6 +865,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the rocprof byte counters)")
     args = ap.parse_args()
+    settle_s = 0.5 if args.warmup is None else 0.0
+    if args.warmup is None:
+        args.warmup = 10
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the layer is measured on a single MI355X (asked for --gpus {args.gpus}); "
               "sharding across GPUs is not part of this library", file=sys.stderr)
@@ -857,7 +887,8 @@ def main():
         return
     tiled = not args.stored_layout
     widths = VERIFIER_WIDTHS if (args.workload == "decode_m8" and not args.no_widths) else None
-    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths, tiled, args.samples)
+    main_res = measure(WORKLOADS[args.workload], args.steps, args.warmup, args.replicas, widths, tiled, args.samples,
+                       settle_s)
     print(f"# {main_res['workload']}: {main_res['ms_per_step'] * 1e3:.1f} us/step, samples {main_res['step_us']}, "
           f"kernels {main_res['kernel_us']}", file=sys.stderr, flush=True)
     if main_res.get("widths"):
@@ -875,7 +906,7 @@ def main():
     for name, st, wu, rep in plan:
         if name == args.workload:
             continue
-        r = measure(WORKLOADS[name], st, wu, rep, tiled=tiled, samples=args.samples)
+        r = measure(WORKLOADS[name], st, wu, rep, tiled=tiled, samples=args.samples, settle_s=settle_s)
         gpu_ids[name] = r.pop("ids").numpy()
         others[name] = leg(r)
         print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, samples {r['step_us']}, kernels "
@@ -913,7 +944,8 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": main_res["warmup_steps"],
+        "warmup_settle_s": settle_s,
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
