@@ -13,7 +13,29 @@
 namespace moe {
 
 constexpr int kPermWaves = 16;
+constexpr int kPermVec = 12;   // 16-byte id vectors per lane and batch: a batch is 3,072 ids per wave
 
+// One batch of a wave's segment: lane l holds ids b0 + 256 u + 4 l .. + 3 in v[u] (-1 past end) for the
+// vectors u that start before end (the others are left as they are and never read). With VEC each vector is
+// one 16-byte load (ids 16-byte aligned); the batch's loads all go out before any is used.
+template <bool VEC>
+__device__ __forceinline__ void load_id_batch(const int32_t* __restrict__ ids, int b0, int end, int lane, int4* v) {
+#pragma unroll
+  for (int u = 0; u < kPermVec; ++u) {
+    if (b0 + 256 * u >= end) break;   // (wave-uniform)
+    const int i = b0 + 256 * u + 4 * lane;
+    if (VEC && i + 4 <= end) {
+      v[u] = *reinterpret_cast<const int4*>(ids + i);
+    } else {
+      v[u].x = i < end ? ids[i] : -1;
+      v[u].y = i + 1 < end ? ids[i + 1] : -1;
+      v[u].z = i + 2 < end ? ids[i + 2] : -1;
+      v[u].w = i + 3 < end ? ids[i + 3] : -1;
+    }
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
@@ -25,36 +47,42 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid < 4) present[tid] = 0ull;
   __syncthreads();
-  // each wave owns a contiguous segment of the pair list (a multiple of 64 long). Block e counts the
-  // pairs of expert e and those of lower experts with wave ballots, and every block collects which ids
-  // occur (a 256-bit mask: its rank among the active experts and their number).
-  const int seg = ((P + kPermWaves * 64 - 1) / (kPermWaves * 64)) * 64;
+  // each wave owns a contiguous segment of the pair list (a multiple of 256 long), read in batches of
+  // kPermVec vectors per lane. Block e counts the pairs of expert e and those of lower experts (per lane,
+  // then over the wave), and every block collects which ids occur (a 256-bit mask: its rank among the
+  // active experts and their number).
+  constexpr int kBatch = 256 * kPermVec;
+  const int seg = ((P + kPermWaves * 256 - 1) / (kPermWaves * 256)) * 256;
   const int beg = wave * seg, end = min(P, beg + seg);
   int mine = 0, lower = 0;
   unsigned long long pm0 = 0ull, pm1 = 0ull, pm2 = 0ull, pm3 = 0ull;
-  constexpr int U = 8;   // ids in flight per lane
-  for (int i0 = beg; i0 < end; i0 += 64 * U) {
-    int v[U];
+  int4 v[kPermVec];
+  auto count = [&](int x) {
+    const bool ok = x >= 0 && x < E;
+    mine += (ok && x == e) ? 1 : 0;
+    lower += (ok && x < e) ? 1 : 0;
+    const unsigned long long bit = ok ? 1ull << (x & 63) : 0ull;
+    const int q = x >> 6;
+    pm0 |= q == 0 ? bit : 0ull;
+    pm1 |= q == 1 ? bit : 0ull;
+    pm2 |= q == 2 ? bit : 0ull;
+    pm3 |= q == 3 ? bit : 0ull;
+  };
+  for (int b0 = beg; b0 < end; b0 += kBatch) {
+    load_id_batch<VEC>(ids, b0, end, lane, v);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + 64 * u + lane;
-      v[u] = i < end ? ids[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = v[u] >= 0 && v[u] < E;
-      mine += __popcll(__ballot(ok && v[u] == e));
-      lower += __popcll(__ballot(ok && v[u] < e));
-      const unsigned long long bit = ok ? 1ull << (v[u] & 63) : 0ull;
-      const int q = v[u] >> 6;
-      pm0 |= q == 0 ? bit : 0ull;
-      pm1 |= q == 1 ? bit : 0ull;
-      pm2 |= q == 2 ? bit : 0ull;
-      pm3 |= q == 3 ? bit : 0ull;
+    for (int u = 0; u < kPermVec; ++u) {
+      if (b0 + 256 * u >= end) break;   // (wave-uniform)
+      count(v[u].x);
+      count(v[u].y);
+      count(v[u].z);
+      count(v[u].w);
     }
   }
-  // OR of the presence words over the wave, then over the block (integer: order-free)
+  // sums and ORs over the wave, then over the block (integer: order-free)
   for (int off = 32; off >= 1; off >>= 1) {
+    mine += __shfl_xor(mine, off, 64);
+    lower += __shfl_xor(lower, off, 64);
     pm0 |= __shfl_xor(pm0, off, 64);
     pm1 |= __shfl_xor(pm1, off, 64);
     pm2 |= __shfl_xor(pm2, off, 64);
@@ -91,27 +119,41 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
     if (e == E - 1) offsets[E] = off + cnt;
   }
   __syncthreads();
+  if (wave_cnt[wave] == 0) return;   // (wave-uniform) no pair of expert e in this segment
   int base = base_off;
   for (int w = 0; w < wave; ++w) base += wave_cnt[w];
+  // stable compaction: pair i goes to base + (hits of expert e before it in the segment). Per vector,
+  // lane l's rank = hits in lanes below l (one ballot per component) + hits in its own earlier components.
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = beg; i0 < end; i0 += 64 * U) {
-    int v[U];
+  for (int b0 = beg; b0 < end; b0 += kBatch) {
+    if (end - beg > kBatch) load_id_batch<VEC>(ids, b0, end, lane, v);   // else: the batch is still in v
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + 64 * u + lane;
-      v[u] = i < end ? ids[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + 64 * u + lane;
-      const bool hit = (v[u] == e);
-      const unsigned long long m = __ballot(hit);
-      if (hit) {
-        const int pos = base + __popcll(m & below);
+    for (int u = 0; u < kPermVec; ++u) {
+      if (b0 + 256 * u >= end) break;   // (wave-uniform)
+      const bool h0 = v[u].x == e, h1 = v[u].y == e, h2 = v[u].z == e, h3 = v[u].w == e;
+      const unsigned long long m0 = __ballot(h0), m1 = __ballot(h1), m2 = __ballot(h2), m3 = __ballot(h3);
+      int pos = base + __popcll(m0 & below) + __popcll(m1 & below) + __popcll(m2 & below) + __popcll(m3 & below);
+      const int i = b0 + 256 * u + 4 * lane;
+      if (h0) {
         pairs[pos] = i;
         if (inv) inv[i] = pos;
+        ++pos;
       }
-      base += __popcll(m);
+      if (h1) {
+        pairs[pos] = i + 1;
+        if (inv) inv[i + 1] = pos;
+        ++pos;
+      }
+      if (h2) {
+        pairs[pos] = i + 2;
+        if (inv) inv[i + 2] = pos;
+        ++pos;
+      }
+      if (h3) {
+        pairs[pos] = i + 3;
+        if (inv) inv[i + 3] = pos;
+      }
+      base += __popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3);
     }
   }
 }
@@ -256,8 +298,10 @@ void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* 
                     int32_t* inv, int32_t* active, hipStream_t s) {
   if (P <= kSmallPairs)
     permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+  else if ((reinterpret_cast<uintptr_t>(ids) & 15u) == 0)
+    permute_kernel<true><<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
   else
-    permute_kernel<<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+    permute_kernel<false><<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
 }
 
 void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,

@@ -130,13 +130,18 @@ def test_qdq_codes_exhaustive_over_bf16():
     assert np.array_equal(xq.cpu().numpy(), codes)
 
 
-@pytest.mark.parametrize("M,k,E,skew", [(8192, 6, 128, False), (37, 6, 128, False), (64, 6, 128, True),
-                                        (4, 2, 8, False), (1, 8, 256, False), (2048, 6, 256, "sparse"),
-                                        (4096, 4, 64, False), (3000, 6, 128, True)])
-def test_permute_is_bit_exact(M, k, E, skew):
+@pytest.mark.parametrize("M,k,E,skew,shift", [(8192, 6, 128, False, 0), (37, 6, 128, False, 0),
+                                              (64, 6, 128, True, 0), (4, 2, 8, False, 0), (1, 8, 256, False, 0),
+                                              (2048, 6, 256, "sparse", 0), (4096, 4, 64, False, 0),
+                                              (3000, 6, 128, True, 0), (1999, 3, 128, False, 0),
+                                              (10000, 6, 128, False, 0), (8192, 6, 128, False, 1),
+                                              (1999, 3, 128, False, 1)])
+def test_permute_is_bit_exact(M, k, E, skew, shift):
     """Counts, offsets, pairs, inverse and the active list, bit for bit against the oracle's counting sort;
     the multi-block kernel (more than 1024 pairs) with every expert, with a sparse set of experts (gaps in
-    the active list) and with all tokens on the same k experts."""
+    the active list), with all tokens on the same k experts, with a pair count that is not a multiple of 4
+    (5,997), with more than one batch of ids per wave (60,000 pairs), and with ids that are 4- but not
+    16-byte aligned (shift 1: the ids start one element into their buffer)."""
     rng = np.random.default_rng(M + E)
     if skew is True:
         ids = np.tile(np.arange(k, dtype=np.int32)[::-1], (M, 1))
@@ -146,7 +151,10 @@ def test_permute_is_bit_exact(M, k, E, skew):
     else:
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(M)]).astype(np.int32)
     dims = m().Dims(E, 256, 128, k)
-    t = torch.from_numpy(ids).cuda()
+    buf = torch.full((M * k + shift,), -7, dtype=torch.int32, device="cuda")
+    t = buf[shift:].view(M, k)
+    t.copy_(torch.from_numpy(ids))
+    assert (t.data_ptr() % 16 == 0) == (shift == 0)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     pairs = torch.empty(M * k, dtype=torch.int32, device="cuda")
