@@ -900,9 +900,9 @@ def main():
     if not args.no_others:
         plan.append(("batched_decode_m64", max(10, args.steps // 2), max(2, args.warmup // 2), args.replicas))
     if not args.no_prefill:
-        plan.append(("prefill_m8192", max(20, args.steps // 5), max(4, args.warmup // 2), 2))
+        plan.append(("prefill_m8192", max(20, args.steps // 5), max(4, args.warmup // 2), args.replicas))
     if not args.no_others:
-        plan.append(("prefill_shared_skew_m2048", max(20, args.steps // 5), max(4, args.warmup // 2), 2))
+        plan.append(("prefill_shared_skew_m2048", max(20, args.steps // 5), max(4, args.warmup // 2), args.replicas))
     for name, st, wu, rep in plan:
         if name == args.workload:
             continue
