@@ -694,19 +694,34 @@ void launch_scales_stage_major(int mats, int N, int K, const uint8_t* s, uint8_t
   scales_stage_major_kernel<<<dim3(N / 64, mats), dim3(256), 0, st>>>(N, K / 32, s, S);
 }
 
-// Thread per (stage q, sorted position): one dword gathered from the token's scale row.
+// Thread per (sorted position, group of four stages): the four dwords of stages 4G .. 4G + 3 of the token's scale
+// row (one 16-byte load when the rows are whole 16-byte units, VEC) go to four stage planes; along a wave the
+// positions are consecutive, so each store is one contiguous 256-byte run.
+template <bool VEC>
 __global__ __launch_bounds__(256) void gather_act_scales_kernel(int P, int k, int q4, const int32_t* __restrict__ pairs,
                                                                 const uint8_t* __restrict__ x_s, uint8_t* __restrict__ out) {
-  const int pos = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
+  const int pos = blockIdx.x * 256 + threadIdx.x, q0 = 4 * blockIdx.y;
   if (pos >= P) return;
   const int t = pairs ? pairs[pos] / k : pos;
-  reinterpret_cast<uint32_t*>(out)[(size_t)q * P + pos] =
-      reinterpret_cast<const uint32_t*>(x_s + (size_t)t * q4 * 4)[q];
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(x_s + (size_t)t * q4 * 4);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(out) + (size_t)q0 * P + pos;
+  if (VEC) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + q0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(size_t)i * P] = v[i];
+  } else {
+    for (int i = 0; i < 4 && q0 + i < q4; ++i) dst[(size_t)i * P] = row[q0 + i];
+  }
 }
 
 void launch_gather_act_scales(int P, int k, int K, const int32_t* pairs, const uint8_t* x_s, uint8_t* out,
                               hipStream_t st) {
-  gather_act_scales_kernel<<<dim3((P + 255) / 256, K / 128), dim3(256), 0, st>>>(P, k, K / 128, pairs, x_s, out);
+  const int q4 = K / 128;   // stages; a scale row is 4 * q4 bytes
+  const dim3 grid((P + 255) / 256, (q4 + 3) / 4);
+  if (q4 % 4 == 0 && (reinterpret_cast<uintptr_t>(x_s) & 15u) == 0)
+    gather_act_scales_kernel<true><<<grid, dim3(256), 0, st>>>(P, k, q4, pairs, x_s, out);
+  else
+    gather_act_scales_kernel<false><<<grid, dim3(256), 0, st>>>(P, k, q4, pairs, x_s, out);
 }
 
 int mfma_max_tiles(int P, int E) { return (P + kTileM - 1) / kTileM + (P < E ? P : E); }

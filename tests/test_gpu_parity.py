@@ -403,8 +403,12 @@ def test_prefill_path_matches_oracle_on_every_token(over, tiled):
         assert_within(res["shared_out"], ref["shared_y"], "shared expert (MFMA path)")
 
 
-def test_prefill_path_h_codes_on_oracle_routing():
-    cfg, inp, d = cfg_inputs(0, M=1000, H=512, I=256, E=8, k=2)
+@pytest.mark.parametrize("I", [256, 640])
+def test_prefill_path_h_codes_on_oracle_routing(I):
+    """The two prefill-width halves as split calls on the oracle's routing: h codes and scales, then the slot
+    outputs from the caller's h. I = 640: five 128-wide K stages of GEMM2 (their scales re-laid in one group of
+    four and one of one) and a partial 256-column tile of GEMM1."""
+    cfg, inp, d = cfg_inputs(0, M=1000, H=512, I=I, E=8, k=2)
     ref = O.moe_forward(inp, cfg)
     M, k, E = cfg.M, cfg.k, cfg.E
     dims = dims_of(cfg)
