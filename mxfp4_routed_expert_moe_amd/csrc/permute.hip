@@ -1,11 +1,11 @@
 // Token-to-expert permutation: a stable counting sort of the M*k (token, slot) pairs by expert id.
 //
 // The expert GEMMs process the rows of one expert together (the grouped layout of the paper
-// "DeepSeek-V4-Flash on AMD gfx90a", section 7.1, and the route-direct chain of the page "DeepSeek V4 Flash REAP/XPU B70 Handoff"); the order inside an expert is
-// ascending pair id t*k + j, so results never depend on scheduling. No global atomics and no
-// in-kernel counter resets: block e counts the pairs of expert e and of the experts below it with wave
-// ballots, finds its rank among the active experts from a presence mask of all ids, and compacts the
-// pairs of expert e with wave ballots.
+// "DeepSeek-V4-Flash on AMD gfx90a", section 7.1, and the route-direct chain of the page "DeepSeek V4 Flash
+// REAP/XPU B70 Handoff"); the order inside an expert is ascending pair id t*k + j, so results never depend on
+// scheduling. No global atomics and no in-kernel counter resets: block e counts the pairs of expert e and of
+// the experts below it (per lane, then over the wave), finds its rank among the active experts from a
+// presence mask of all ids, and compacts the pairs of expert e with wave ballots.
 #include "kernels.h"
 #include "moe_device.h"
 #include "route_device.h"
