@@ -37,7 +37,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // One wave selects the experts of token t from the partial logit planes [nparts][M][E] (added in
-// ascending plane order). Lane 0 writes ids[t * k + r] and rw[t * k + r] (r = rank, descending
+// ascending plane order). Lane r writes ids[t * k + r] and rw[t * k + r] (r = rank, descending
 // selection score); when sid is given, the ids to sid[t * k + r] too, and when emask is given (t < 64)
 // it sets bit t of emask[id] for each chosen expert. The k ids of a token are distinct. k <= 8; NJ experts
 // per lane, E <= 64 * NJ (NJ = 2 for E <= 128 halves the per-lane work; the decisions do not depend on NJ).
@@ -110,21 +110,26 @@ __device__ __forceinline__ void select_token(int t, int M, int E, int k, float r
     for (int j = 0; j < NJ; ++j)
       if (lane + 64 * j == win) key[j] = 0u;   // remove the winner
   }
-  if (lane == 0) {
-    float sum = 0.0f;
+  // the selected scores are wave-uniform, so every lane forms the same normalising sum (slot order); lane r < k
+  // then writes slot r
+  float sum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (r < k) sum = sum + wsel[r];
-    const float denom = sum + 1e-20f;
+  for (int r = 0; r < 8; ++r)
+    if (r < k) sum = sum + wsel[r];
+  const float denom = sum + 1e-20f;
+  if (lane < k) {
+    float wv = wsel[0];
+    int iv = isel[0];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (r < k) {
-        ids[(size_t)t * k + r] = isel[r];
-        rw[(size_t)t * k + r] = (wsel[r] / denom) * route_scale;
-        if (sid != nullptr) sid[t * k + r] = isel[r];
-        if (emask != nullptr) atomicOr(&emask[isel[r]], 1ull << t);
+    for (int r = 1; r < 8; ++r)
+      if (lane == r) {
+        wv = wsel[r];
+        iv = isel[r];
       }
-    }
+    ids[(size_t)t * k + lane] = iv;
+    rw[(size_t)t * k + lane] = (wv / denom) * route_scale;
+    if (sid != nullptr) sid[t * k + lane] = iv;
+    if (emask != nullptr) atomicOr(&emask[iv], 1ull << t);
   }
 }
 
