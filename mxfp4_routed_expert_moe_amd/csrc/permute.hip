@@ -247,24 +247,19 @@ __global__ __launch_bounds__(1024) void select_permute_small_kernel(
   __syncthreads();
   if (wave == 0) {   // counts, offsets and the active list: lane l owns experts 4l .. 4l + 3
     int c[4], csum = 0, fsum = 0;
+    unsigned long long em[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) em[i] = emask[4 * lane + i];   // all four reads in flight (256 entries)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      c[i] = e < E ? __popcll(emask[e]) : 0;
+      c[i] = e < E ? __popcll(em[i]) : 0;
       csum += c[i];
       fsum += c[i] > 0 ? 1 : 0;
     }
-    int ic = csum, ifl = fsum;   // inclusive scans over the lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int a = __shfl_up(ic, off, 64), b = __shfl_up(ifl, off, 64);
-      if (lane >= off) {
-        ic += a;
-        ifl += b;
-      }
-    }
+    const int ic = wave_incl_scan(csum), ifl = wave_incl_scan(fsum);   // inclusive scans over the lanes
     int oc = ic - csum, of = ifl - fsum;
-    const int total = __shfl(ic, 63, 64), n_active = __shfl(ifl, 63, 64);
+    const int total = __builtin_amdgcn_readlane(ic, 63), n_active = __builtin_amdgcn_readlane(ifl, 63);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;

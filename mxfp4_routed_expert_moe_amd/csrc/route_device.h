@@ -36,6 +36,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(m01, m23);
 }
 
+// Inclusive prefix sum of a 32-bit value over the 64 lanes of the wave, on DPP: inside each 16-lane row by
+// shifts of 1, 2, 4 and 8 lanes (lanes past the row's start add 0), then across rows by adding lane 15 to rows 1
+// and 3 and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // One wave selects the experts of token t from the partial logit planes [nparts][M][E] (added in
 // ascending plane order). Lane r writes ids[t * k + r] and rw[t * k + r] (r = rank, descending
 // selection score); when sid is given, the ids to sid[t * k + r] too, and when emask is given (t < 64)
