@@ -72,17 +72,13 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
 #pragma unroll
     for (int u = 0; u < 4; ++u) a[u] = dot8(t + u);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] += __shfl_xor(a[u], off, 64);
+    for (int u = 0; u < 4; ++u) a[u] = wave_sum_lane0(a[u]);   // the butterfly, as lane 0 forms it
     if (lane == 0)
 #pragma unroll
       for (int u = 0; u < 4; ++u) part[(size_t)chunk * plane + (size_t)(t + u) * E + e] = a[u];
   }
   for (; t < M; ++t) {
-    float a = dot8(t);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
+    const float a = wave_sum_lane0(dot8(t));
     if (lane == 0) part[(size_t)chunk * plane + (size_t)t * E + e] = a;
   }
 }

@@ -36,6 +36,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(m01, m23);
 }
 
+// Lane 0's value after an xor butterfly over the 64 lanes (offsets 32, 16, 8, 4, 2, 1 in that order, each step
+// a += a[lane ^ offset]), with the same bits. Offsets 32 and 16 are lane permutes; for 8, 4, 2 and 1, every lane
+// that lane 0's sum depends on has lane < offset, so its partner lane ^ offset = lane + offset lies in the same
+// 16-lane row and a DPP row shift reads it. Only lane 0's result is meaningful.
+__device__ __forceinline__ float wave_sum_lane0(float a) {
+  a += __shfl_xor(a, 32, 64);
+  a += __shfl_xor(a, 16, 64);
+  a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x108, 0xF, 0xF, true));   // row_shl:8
+  a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x104, 0xF, 0xF, true));   // row_shl:4
+  a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x102, 0xF, 0xF, true));   // row_shl:2
+  a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x101, 0xF, 0xF, true));   // row_shl:1
+  return a;
+}
+
 // Inclusive prefix sum of a 32-bit value over the 64 lanes of the wave, on DPP: inside each 16-lane row by
 // shifts of 1, 2, 4 and 8 lanes (lanes past the row's start add 0), then across rows by adding lane 15 to rows 1
 // and 3 and lane 31 to rows 2 and 3.
