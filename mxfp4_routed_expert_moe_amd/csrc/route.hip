@@ -50,11 +50,14 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
   if (e >= E) return;
   const size_t plane = (size_t)M * E;
   // one token's partial: an 8-FMA chain per lane, then a butterfly over the 64 lanes. Four tokens at a
-  // time, so that their butterflies overlap (each token's order is unchanged).
-  auto dot8 = [&](int t) {
+  // time, so that their butterflies overlap, and the x slices of the next four are loaded before the current
+  // four are added up (each token's order is unchanged).
+  auto xload = [&](int t) {
+    return (ok && t < M) ? *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto dot8v = [&](const u32x4& xv) {
     float a = 0.0f;
     if (ok) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(x + (size_t)t * H + h);
       a = __builtin_fmaf(bits_to_f32(xv[0] << 16), w0.x, a);
       a = __builtin_fmaf(bits_to_f32(xv[0] & 0xFFFF0000u), w0.y, a);
       a = __builtin_fmaf(bits_to_f32(xv[1] << 16), w0.z, a);
@@ -66,20 +69,30 @@ __global__ __launch_bounds__(256) void router_logits_small(int M, int H, int E, 
     }
     return a;
   };
+  u32x4 xn[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) xn[u] = xload(u);
   int t = 0;
   for (; t + 4 <= M; t += 4) {
+    u32x4 xc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xc[u] = xn[u];
+      xn[u] = xload(t + 4 + u);   // the next group (zeros past M)
+    }
     float a[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = dot8(t + u);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = wave_sum_lane0(a[u]);   // the butterfly, as lane 0 forms it
+    for (int u = 0; u < 4; ++u) a[u] = wave_sum_lane0(dot8v(xc[u]));   // the butterfly, as lane 0 forms it
     if (lane == 0)
 #pragma unroll
       for (int u = 0; u < 4; ++u) part[(size_t)chunk * plane + (size_t)(t + u) * E + e] = a[u];
   }
-  for (; t < M; ++t) {
-    const float a = wave_sum_lane0(dot8(t));
-    if (lane == 0) part[(size_t)chunk * plane + (size_t)t * E + e] = a;
+  // the last M % 4 tokens: their slices are in xn[0 .. M % 4 - 1]
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    if (t + u >= M) break;
+    const float a = wave_sum_lane0(dot8v(xn[u]));
+    if (lane == 0) part[(size_t)chunk * plane + (size_t)(t + u) * E + e] = a;
   }
 }
 
