@@ -29,7 +29,8 @@ void launch_router_select_qdq(int M, int H, int E, int k, float route_scale, con
                               uint8_t* x_q, uint8_t* x_s, bool mfma_order, hipStream_t s);
 
 // ---- permutation (permute.hip) -------------------------------------------------------------
-// Stable counting sort of the M*k (token, slot) pairs by expert id.
+// Stable counting sort of the M*k (token, slot) pairs by expert id. active may be null (no active list: for
+// callers whose expert GEMMs read the row-tile map).
 void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                     int32_t* pairs, int32_t* inv, int32_t* active, hipStream_t s);
 // M <= kRouterSmallM only: the router's selection (from the partial logit planes) and the counting sort in

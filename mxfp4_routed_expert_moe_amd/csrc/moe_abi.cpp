@@ -420,8 +420,9 @@ void forward_impl(const moe_dims* dims, int32_t M, const uint16_t* x, const floa
                                      at<int32_t>(ws, L.inv), active, at<int32_t>(ws, L.out_rows), s);
   } else {
     do_route(dims, M, x, gate_w, gate_b, ids, rw, xq, xs, ws, s);
+    // at the row-tiled widths the expert GEMMs read the row-tile map, so the active list is not built
     moe::launch_permute(M * dims->top_k, dims->num_experts, ids, at<int32_t>(ws, L.counts), offsets, pairs,
-                        at<int32_t>(ws, L.inv), active, s);
+                        at<int32_t>(ws, L.inv), routed_tiled(dims, M) ? nullptr : active, s);
   }
   uint16_t* slot = at<uint16_t>(ws, L.slot);
   uint16_t* sh_out = shared != nullptr ? (shared_out ? shared_out : at<uint16_t>(ws, L.sh_out)) : nullptr;

@@ -35,7 +35,9 @@ __device__ __forceinline__ void load_id_batch(const int32_t* __restrict__ ids, i
   }
 }
 
-template <bool VEC>
+// ACTIVE = false (active == nullptr: a caller whose expert GEMMs read the row-tile map instead): no presence
+// mask and no active list, a third less work per id.
+template <bool VEC, bool ACTIVE>
 __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ pairs, int32_t* __restrict__ inv,
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
     const bool ok = x >= 0 && x < E;
     mine += (ok && x == e) ? 1 : 0;
     lower += (ok && x < e) ? 1 : 0;
+    if constexpr (!ACTIVE) return;
     const unsigned long long bit = ok ? 1ull << (x & 63) : 0ull;
     const int q = x >> 6;
     pm0 |= q == 0 ? bit : 0ull;
@@ -83,18 +86,22 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
   for (int off = 32; off >= 1; off >>= 1) {
     mine += __shfl_xor(mine, off, 64);
     lower += __shfl_xor(lower, off, 64);
-    pm0 |= __shfl_xor(pm0, off, 64);
-    pm1 |= __shfl_xor(pm1, off, 64);
-    pm2 |= __shfl_xor(pm2, off, 64);
-    pm3 |= __shfl_xor(pm3, off, 64);
+    if constexpr (ACTIVE) {
+      pm0 |= __shfl_xor(pm0, off, 64);
+      pm1 |= __shfl_xor(pm1, off, 64);
+      pm2 |= __shfl_xor(pm2, off, 64);
+      pm3 |= __shfl_xor(pm3, off, 64);
+    }
   }
   if (lane == 0) {
     wave_cnt[wave] = mine;
     wave_below[wave] = lower;
-    atomicOr(&present[0], pm0);
-    atomicOr(&present[1], pm1);
-    atomicOr(&present[2], pm2);
-    atomicOr(&present[3], pm3);
+    if constexpr (ACTIVE) {
+      atomicOr(&present[0], pm0);
+      atomicOr(&present[1], pm1);
+      atomicOr(&present[2], pm2);
+      atomicOr(&present[3], pm3);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -106,16 +113,17 @@ __global__ __launch_bounds__(1024) void permute_kernel(int P, int E, const int32
     base_off = off;
     counts[e] = cnt;
     offsets[e] = off;
-    // rank of e among the active experts (ascending id), and their number
-    int rank = 0, n_active = 0;
-    for (int q = 0; q < 4; ++q) {
-      const unsigned long long m = present[q];
-      n_active += __popcll(m);
-      if (64 * q + 63 < e) rank += __popcll(m);
-      else if (64 * q <= e) rank += __popcll(m & ((1ull << (e & 63)) - 1ull));
+    if constexpr (ACTIVE) {   // rank of e among the active experts (ascending id), and their number
+      int rank = 0, n_active = 0;
+      for (int q = 0; q < 4; ++q) {
+        const unsigned long long m = present[q];
+        n_active += __popcll(m);
+        if (64 * q + 63 < e) rank += __popcll(m);
+        else if (64 * q <= e) rank += __popcll(m & ((1ull << (e & 63)) - 1ull));
+      }
+      if (cnt > 0) active[rank] = e;   // positions < n_active
+      if (e >= n_active) active[e] = -1;   // padding: positions >= n_active, disjoint from the above
     }
-    if (cnt > 0) active[rank] = e;   // positions < n_active
-    if (e >= n_active) active[e] = -1;   // padding: positions >= n_active, disjoint from the above
     if (e == E - 1) offsets[E] = off + cnt;
   }
   __syncthreads();
@@ -199,8 +207,10 @@ __device__ __forceinline__ void counting_sort_small(int P, int E, int v, int* si
     const int c = hist[tid];
     counts[tid] = c;
     offsets[tid] = scan[tid] - c;
-    if (c > 0) active[ascan[tid] - 1] = tid;   // positions < n_active
-    if (tid >= n_active) active[tid] = -1;      // padding: positions >= n_active, disjoint from the above
+    if (active != nullptr) {
+      if (c > 0) active[ascan[tid] - 1] = tid;   // positions < n_active
+      if (tid >= n_active) active[tid] = -1;      // padding: positions >= n_active, disjoint from the above
+    }
   }
   if (tid == 0) offsets[E] = scan[255];
   if (ok) {
@@ -293,10 +303,14 @@ void launch_permute(int P, int E, const int32_t* ids, int32_t* counts, int32_t* 
                     int32_t* inv, int32_t* active, hipStream_t s) {
   if (P <= kSmallPairs)
     permute_small_kernel<<<dim3(1), dim3(kSmallPairs), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
-  else if ((reinterpret_cast<uintptr_t>(ids) & 15u) == 0)
-    permute_kernel<true><<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
-  else
-    permute_kernel<false><<<dim3(E), dim3(kPermWaves * 64), 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+  else {
+    const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15u) == 0;
+    const dim3 g(E), b(kPermWaves * 64);
+    if (vec && active) permute_kernel<true, true><<<g, b, 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+    else if (vec) permute_kernel<true, false><<<g, b, 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+    else if (active) permute_kernel<false, true><<<g, b, 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+    else permute_kernel<false, false><<<g, b, 0, s>>>(P, E, ids, counts, offsets, pairs, inv, active);
+  }
 }
 
 void launch_select_permute_small(int M, int H, int E, int k, float route_scale, const float* logits,
