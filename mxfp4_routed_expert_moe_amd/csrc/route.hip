@@ -131,8 +131,8 @@ __device__ __forceinline__ void split_gate8(const f32x4& lo4, const f32x4& hi4, 
 // steps ahead; per wave one x copy (16 rows) and two gate copies (8 rows each). The 16-byte chunks of each
 // LDS row are XOR-swizzled (x: chunk ^ ((r ^ r >> 2) & 3); gate: chunk ^ (r & 7)) so that the 16 rows of a
 // fragment read distinct banks.
-// Wave w computes tokens 64 (w / 4) .. + 63 (four A tiles) x experts 32 (w % 4) .. + 31 (two B tiles):
-// per step and tile the hi, mid and lo products, in that order (v_mfma_f32_16x16x32_bf16: lane l
+// Wave w computes all 128 tokens (eight A tiles) x experts 16 w .. + 15 (one B tile, so each gate fragment is
+// split once per block): per step and tile the hi, mid and lo products, in that order (v_mfma_f32_16x16x32_bf16: lane l
 // supplies row l % 16 of A and column l % 16 of B, inputs 8 (l / 16) .. + 7 of the step; the result
 // (4 (l / 16) + v, l % 16) is accumulator v of lane l).
 constexpr int kRtStages = 3;
@@ -170,12 +170,10 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
 #pragma unroll
     for (int c = 0; c < 2; ++c) copy16(gsrc[c] + h, &st.g[(16 * wave + 8 * c) * 32]);
   };
-  const int th = wave >> 2, eq = wave & 3;
-  f32x4 acc[4][2];
+  // wave w: experts 16 w .. 16 w + 15 (one B fragment, split once per block) for all 128 tokens
+  f32x4 acc[8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < 8; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   issue(0);
   if (nk > 1) issue(1);
   for (int s = 0; s < nk; ++s) {
@@ -184,39 +182,33 @@ __global__ __launch_bounds__(512, 1) void router_logits_mfma(int M, int H, int E
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (s + 2 < nk) issue(s + 2);   // into the slot read at step s - 1: every wave is past it
     const RouterStage& st = ring[s % kRtStages];
-    u32x4 A[4], B[2][3];
+    u32x4 A[8], B[3];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int r = 64 * th + 16 * a + r16;
+    for (int a = 0; a < 8; ++a) {
+      const int r = 16 * a + r16;
       A[a] = *reinterpret_cast<const u32x4*>(&st.x[r * 32 + 8 * (g ^ rt_key(r))]);
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int r = 32 * eq + 16 * b + r16;
+    {
+      const int r = 16 * wave + r16;
       const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&st.g[r * 32 + 4 * ((2 * g) ^ (r & 7))]);
       const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&st.g[r * 32 + 4 * ((2 * g + 1) ^ (r & 7))]);
-      split_gate8(lo4, hi4, B[b][0], B[b][1], B[b][2]);
+      split_gate8(lo4, hi4, B[0], B[1], B[2]);
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[a]),
-                                                             __builtin_bit_cast(bf16x8, B[b][q]), acc[a][b], 0, 0, 0);
+      for (int q = 0; q < 3; ++q)
+        acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[a]),
+                                                         __builtin_bit_cast(bf16x8, B[q]), acc[a], 0, 0, 0);
   }
   float* out = part + (size_t)blockIdx.y * M * E;
+  const int e = e0 + 16 * wave + r16;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int e = e0 + 32 * eq + 16 * b + r16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = t0 + 64 * th + 16 * a + 4 * g + v;
-        if (t < M && e < E) out[(size_t)t * E + e] = acc[a][b][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + 16 * a + 4 * g + v;
+      if (t < M && e < E) out[(size_t)t * E + e] = acc[a][v];
     }
 }
 
