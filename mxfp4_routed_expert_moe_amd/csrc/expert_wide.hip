@@ -19,7 +19,8 @@
 //
 // Data flow. Each weight row is used by one wave only, so the weights go straight from the fragment-order
 // copy into registers (one 1 KB contiguous load per 16-row fragment and step), two steps ahead of their use
-// in three rotating register sets. The activation rows (shared by the four waves) and the E8M0 bytes of both
+// in three rotating register sets; in a full tile the eight loads of a step go out one between each group of
+// eight MFMAs. The activation rows (shared by the four waves) and the E8M0 bytes of both
 // operands go into a three-slot LDS ring by direct global-to-LDS copies, two steps ahead. The activation
 // copies place each 16-row fragment in the order its MFMA lanes read it, so every fragment read is one
 // conflict-free 16-byte read per lane and half. Every wave issues the same five copies and eight loads per
@@ -219,9 +220,11 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
   };
   // the 64 MFMAs of one step; the B fragments are read one ahead, and after the last one the head of the
   // next step (whose copies have landed: the wait at the top of this step covered them)
-  auto compute = [&](auto slot, auto set, auto part) {
+  auto compute = [&](int s, auto slot, auto set, auto part) {
     constexpr int S = decltype(slot)::value, R = decltype(set)::value;
     constexpr bool PART = decltype(part)::value;
+    constexpr int RN = (S + kAAhead) % kASets;   // register set of step s + 2 (a full tile loads it here)
+    const uint32_t jn = (uint32_t)min(s + kAAhead, nk - 1);
     i32x8 Af[8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
@@ -242,6 +245,7 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
       } else if (!PART) {
         read_head(Int<(S + 1) % kSlots>{});
       }
+      if constexpr (!PART) A[RN][b] = load16((GEMM1 && b >= 4) ? wrb : wra, aoff, afrag[b] + jn * 1024u);
 #pragma unroll
       for (int a = 0; a < 8; ++a)
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af[a], Bf, acc[a][b], 4, 0, 0, sac[a], 0, sbc);
@@ -250,13 +254,17 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
       read_head(Int<(S + 1) % kSlots>{});
     } else {
       // schedule: the reads of B fragment b + 1 (three LDS reads; after the last fragment the eleven reads of
-      // the next step's head), then the eight MFMAs of fragment b, which hide their latency
+      // the next step's head), weight load b of step s + 2, then the eight MFMAs of fragment b, which hide
+      // their latency. (The eight weight loads issued together stall the wave's issue, MFMAs included,
+      // while the memory pipeline takes them in.)
 #pragma unroll
       for (int b = 0; b < 7; ++b) {
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 11, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
   };
@@ -271,8 +279,13 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
     __builtin_amdgcn_s_barrier();      // every wave's copies for s + 1 are visible; slot s - 1 is free
     asm volatile("" ::: "memory");
     copies(s + kBAhead, Int<(S + kBAhead) % kSlots>{});
-    loads(s + kAAhead, Int<(S + kAAhead) % kASets>{});
-    if (s < nk) compute(slot, Int<S % kASets>{}, part);
+    asm volatile("" ::: "memory");     // (the weight loads stay behind the copies: the waits count on that order)
+    // the weight loads of step s + 2: a full tile's between the MFMAs of step s, a partial tile's (whose
+    // fragment loop branches) and those of a step past the end here
+    constexpr bool PART = decltype(part)::value;
+    if constexpr (PART) loads(s + kAAhead, Int<(S + kAAhead) % kASets>{});
+    if (s < nk) compute(s, slot, Int<S % kASets>{}, part);
+    else if constexpr (!PART) loads(s + kAAhead, Int<(S + kAAhead) % kASets>{});
   };
 
   // the epilogue's per-row data (pair id, route weight) is fetched now, under the prologue's wait, and kept
@@ -301,7 +314,6 @@ __global__ __launch_bounds__(256, 1) void expert_gemm_wide(GemmProblem p, const 
       step(s, Int<0>{}, part);
       step(s + 1, Int<1>{}, part);
       step(s + 2, Int<2>{}, part);
-
     }
   };
   static_assert(kGroup == 3, "loop group");
