@@ -45,7 +45,7 @@ WORKLOADS = {"tiny_m4": 0, "decode_m8": 1, "batched_decode_m64": 2, "prefill_m81
 FETCH_SCALE, WRITE_SCALE = 1048576 / 524300.9, 1.0
 MEASURED_TRAFFIC = {
     "decode_m8": dict(src="expert_gemm.hip", sha="9d186bd42894c2f5", fetch_kib=227911.2, write_kib=135.1),
-    "prefill_m8192": dict(src="expert_wide.hip", sha="ad57f8a5cc8577ce", fetch_kib=1507187.5, write_kib=114373.6),
+    "prefill_m8192": dict(src="expert_wide.hip", sha="e3b50cc018fcb773", fetch_kib=1492984.0, write_kib=114324.0),
 }
 
 
